@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the paged KV-cache hot path on one MI355X.
+
+A step is one pass of the path over one synthetic batch, all on one stream:
+  * Qwen3-0.6B-shaped decode layer (the headline workload, default): pa_store_kv
+    of the 256 sequences' newest tokens, then pa_decode over their paged
+    contexts (U[100,1024] tokens, 16 Q / 8 KV heads, head_dim 128, block 256);
+  * the mixed chunked-prefill step (--workload 4): pa_store_kv of 4344 new
+    tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
+    of 248 sequences.
+Inputs are resident in HBM before the timed region. `value` is the step's
+algorithmic bytes (unique KV bytes read by decode and prefill, q/out, tables,
+plus the store's reads and writes) divided by the wall time per step. The
+`roofline` object is the dominant call (pa_decode) timed with HIP events on
+the stream it runs on. `cpu_baseline` times the CPU oracle (numpy float64) on
+a bounded sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 2]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_TBS = 8.0              # MI355X HBM3E, TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work
+def decode_bytes(w, seqs=None):
+    """Algorithmic bytes of one pa_decode: K and V of every valid token of every
+    *unique* (physical block, KV head) read, plus q, out, the table entries read
+    and the context lengths (plus fp8 scales). Also returns the logical KV bytes
+    (shared blocks counted once per sequence that reads them)."""
+    es = 1 if w.kv_dtype == "fp8" else 2
+    row = w.num_kv_heads * w.head_dim * es * 2         # K+V bytes of one token, all KV heads
+    seqs = range(w.num_seqs) if seqs is None else seqs
+    unique = {}
+    logical = 0
+    entries = 0
+    for s in seqs:
+        n = int(w.context_lens[s])
+        nb = math.ceil(n / w.block_size)
+        entries += nb
+        logical += n * row
+        for j in range(nb):
+            b = int(w.block_tables[s, j])
+            unique[b] = max(unique.get(b, 0), min(w.block_size, n - j * w.block_size))
+    kv_unique = sum(unique.values()) * row
+    S = len(list(seqs)) if not isinstance(seqs, range) else len(seqs)
+    extra = 2 * S * w.num_q_heads * w.head_dim * 2 + 4 * entries + 4 * S
+    if w.kv_dtype == "fp8":
+        extra += 2 * 4 * w.num_kv_heads
+    return kv_unique + extra, logical + extra, kv_unique
+
+
+def store_bytes(w):
+    """k, v read (bf16) + slots read + pool bytes written."""
+    T = w.new_slots.size
+    es = 1 if w.kv_dtype == "fp8" else 2
+    return T * w.num_kv_heads * w.head_dim * (2 * 2 + 2 * es) + 4 * T
+
+
+def prefill_work(w):
+    """(flops, bytes): 4*D*Hq per unmasked (query, key) pair (QK^T and PV), and the
+    K/V of each sequence's Lk keys + q + out + table entries + cu_seqlens."""
+    cu_q, cu_k = w.cu_seqlens_q, w.cu_seqlens_k
+    pairs = 0
+    kv = 0
+    entries = 0
+    for s in range(len(cu_q) - 1):
+        lq = int(cu_q[s + 1] - cu_q[s])
+        lk = int(cu_k[s + 1] - cu_k[s])
+        pairs += sum(lk - lq + i + 1 for i in range(lq))
+        kv += lk * w.num_kv_heads * w.head_dim * 2 * 2
+        entries += math.ceil(lk / w.block_size)
+    tq = int(cu_q[-1])
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    byts = kv + 2 * tq * w.num_q_heads * w.head_dim * 2 + 4 * entries + 8 * (len(cu_q))
+    return flops, byts
+
+
+# ---------------------------------------------------------------- GPU set-up
+class Setup:
+    def __init__(self, w):
+        import torch
+
+        import paged_kv_cache_store_amd as pa
+        import workloads as W
+        self.w, self.pa, self.torch = w, pa, torch
+
+        def dev_bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+        def dev_i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+        self.kc, self.vc = pa.empty_pools(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim,
+                                          w.kv_dtype)
+        self.ks = self.vs = None
+        if w.kv_dtype == "fp8":
+            self.kc.fill_(int(W.FP8_NAN))
+            self.vc.fill_(int(W.FP8_NAN))
+            self.ks = torch.from_numpy(w.k_scale).cuda()
+            self.vs = torch.from_numpy(w.v_scale).cuda()
+        else:
+            self.kc.view(torch.int16).fill_(int(W.BF16_NAN))
+            self.vc.view(torch.int16).fill_(int(W.BF16_NAN))
+        # cached context, written once before timing (in slices to bound host memory)
+        step = 1 << 18
+        for lo in range(0, w.fill_slots.size, step):
+            hi = min(w.fill_slots.size, lo + step)
+            pa.store_kv(dev_bf16(w.fill_k[lo:hi]), dev_bf16(w.fill_v[lo:hi]),
+                        dev_i32(w.fill_slots[lo:hi]), self.kc, self.vc, self.ks, self.vs)
+        self.new_k, self.new_v = dev_bf16(w.new_k), dev_bf16(w.new_v)
+        self.new_slots = dev_i32(w.new_slots)
+        self.q = dev_bf16(w.q)
+        self.bt = dev_i32(w.block_tables)
+        self.lens = dev_i32(w.context_lens)
+        self.out = torch.empty_like(self.q)
+        self.P = pa.decode_partition_size(w.num_seqs, w.num_q_heads, w.max_context_len, w.partition_size)
+        need = pa.decode_workspace_size(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len, self.P)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        if w.has_prefill:
+            self.pq = dev_bf16(w.pq)
+            self.cu_q, self.cu_k = dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k)
+            self.pbt = dev_i32(w.p_block_tables)
+            self.pout = torch.empty_like(self.pq)
+        torch.cuda.synchronize()
+
+    def store(self):
+        self.pa.store_kv(self.new_k, self.new_v, self.new_slots, self.kc, self.vc, self.ks, self.vs)
+
+    def decode(self):
+        w = self.w
+        self.pa.decode(self.q, self.kc, self.vc, self.bt, self.lens, float(w.scale), w.max_context_len,
+                       out=self.out, k_scale=self.ks, v_scale=self.vs, partition_size=self.P,
+                       workspace=self.ws)
+
+    def prefill(self):
+        w = self.w
+        self.pa.prefill_varlen(self.pq, self.kc, self.vc, self.cu_q, self.cu_k, self.pbt, float(w.scale),
+                               w.max_seqlen_q, w.max_seqlen_k, out=self.pout)
+
+
+def run_steps(st, steps, warmup):
+    """Warm up, then time `steps` steps; per-call HIP events on the launch stream."""
+    torch = st.torch
+    calls = [("store", st.store)]
+    if st.w.has_prefill:
+        try:
+            st.prefill()
+            calls.append(("prefill", st.prefill))
+        except st.pa.PaError as e:          # prefill kernel not in this build
+            log(f"[bench] prefill skipped: {e}")
+    calls.append(("decode", st.decode))
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    stream = torch.cuda.current_stream()
+    ev = {name: [] for name, _ in calls}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, f in calls:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
+    return (t1 - t0) * 1e3 / steps, ms
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+def _oracle_baseline(w, budget_s=12.0):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    ks, vs = oracle.cache.pool_shapes(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
+    dt = np.uint8 if w.kv_dtype == "fp8" else np.uint16
+    kc, vc = np.zeros(ks, dt), np.zeros(vs, dt)
+    oracle.cache.store(w.fill_k, w.fill_v, w.fill_slots, kc, vc, w.block_size, w.k_scale, w.v_scale)
+    done = 0
+    passes = 0
+    nbytes = 0
+    t_total = 0.0
+    while t_total < budget_s and passes < 50:
+        chunk = np.arange(done % w.num_seqs, min(w.num_seqs, done % w.num_seqs + 16))
+        last = [int(w.block_tables[s, (int(w.context_lens[s]) - 1) // w.block_size]) * w.block_size
+                + (int(w.context_lens[s]) - 1) % w.block_size for s in chunk]
+        sel = np.isin(w.new_slots, last)
+        t0 = time.perf_counter()
+        oracle.cache.store(w.new_k[sel], w.new_v[sel], w.new_slots[sel], kc, vc, w.block_size,
+                           w.k_scale, w.v_scale)
+        oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.block_size,
+                                w.k_scale, w.v_scale, seqs=chunk)
+        t_total += time.perf_counter() - t0
+        nbytes += decode_bytes(w, chunk)[0]
+        done += len(chunk)
+        if done % w.num_seqs == 0:
+            passes += 1
+    return {"value": nbytes / t_total / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} sequence decodes ({done / w.num_seqs:.2f} passes over the "
+                      f"{w.num_seqs} sequences of the same workload; store of each newest token + "
+                      f"decode), {t_total:.1f} s of work",
+            "seconds": round(t_total, 2)}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="decode partition size (default: the workload's, else automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("this build runs on one GPU only: --gpus must be 1 (no multi-GPU path exists)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    def measure(number, steps, warmup):
+        w = W.make(number)
+        if args.partition_size is not None:
+            w.partition_size = args.partition_size
+        st = Setup(w)
+        ms_step, ms = run_steps(st, steps, warmup)
+        dec_b, dec_logical, dec_kv = decode_bytes(w)
+        res = {"w": w, "ms_step": ms_step, "ms": ms, "decode_bytes": dec_b,
+               "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P}
+        if w.has_prefill:
+            res["prefill_flops"], res["prefill_bytes"] = prefill_work(w)
+        del st
+        torch.cuda.empty_cache()
+        return res
+
+    log(f"[bench] workload {args.workload}: generating + set-up")
+    r = measure(args.workload, args.steps, args.warmup)
+    w = r["w"]
+    step_bytes = r["decode_bytes"] + r["store_bytes"] + r.get("prefill_bytes", 0)
+    value = step_bytes / (r["ms_step"] * 1e-3) / 1e12
+    dec_tbs = r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12
+    line = {
+        "metric": "paged-attn decode KV TB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
+        "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
+        "data": "synthetic (seeded; bf16 N(0,1) q/k/v, random block permutation)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
+                                   f"mean {float(w.context_lens.mean()):.1f}",
+                   "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (decode + LSE reduce)",
+                     "achieved": round(dec_tbs * 1e3, 2), "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
+                     "frac": round(dec_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
+        "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
+    }
+    if not args.no_extra:
+        extra = {}
+        for number in [n for n in (3, 4, 5) if n != args.workload]:
+            log(f"[bench] workload {number}")
+            e = measure(number, max(5, args.steps // 2), 2)
+            ent = {"decode_TBps": round(e["decode_bytes"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),
+                   "decode_ms": round(e["ms"]["decode"], 5), "decode_unique_bytes": e["decode_bytes"],
+                   "decode_logical_TBps": round(e["decode_logical"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),
+                   "store_ms": round(e["ms"]["store"], 5), "partition_size": e["P"]}
+            if "prefill" in e["ms"]:
+                tf = e["prefill_flops"] / (e["ms"]["prefill"] * 1e-3) / 1e12
+                ent.update({"prefill_TFLOPs": round(tf, 2), "prefill_ms": round(e["ms"]["prefill"], 5),
+                            "prefill_frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                            "prefill_flops": e["prefill_flops"]})
+            extra[e["w"].name] = ent
+        line["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = _oracle_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

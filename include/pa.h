@@ -1,0 +1,169 @@
+/*
+ * pa.h — C ABI of the paged KV-cache attention library (libpa.so, gfx950).
+ *
+ * The operations come from the pages' description of PagedAttention:
+ *  - the KV cache is cut into fixed-size blocks stored non-contiguously in one
+ *    pool ("nano-vllm：轻量级大模型推理引擎的技术探索与实践", PagedAttention 原理回顾;
+ *    "Nano-vLLM：轻量高效的大模型推理框架…", 三.1 推理引擎架构, 块管理器);
+ *  - a per-sequence block table maps logical blocks to physical blocks, and
+ *    blocks may be shared within and across requests ("DeepSeek复刻vLLM反超原版：
+ *    AI推理新标杆", section vLLM：大模型推理的加速引擎与挑战; prefix caching in
+ *    "Nano-vLLM…", 三.2 (1) 前缀缓存);
+ *  - attention is exact, memory-efficient ("FlashAttention idea", "Nano-vLLM…",
+ *    三.3 模型层适配); decode is bound by KV-cache reads and prefill by compute,
+ *    and prefill may come in chunks mixed with decode ("nano-vllm-lite：深入理解
+ *    LLM推理机制的教育级开源项目", 核心技术改进 §2 Chunked Prefill);
+ *  - the KV cache may be stored as FP8 with 2x compression (same page, §3).
+ *
+ * Conventions common to every call
+ *  - Ownership: the caller owns all memory. Every pointer marked "device" is
+ *    device memory on the device that owns `stream`; "host" pointers are read
+ *    during the call only. The library allocates nothing, frees nothing and
+ *    keeps no pointer after returning.
+ *  - Asynchrony: all GPU work is enqueued on `stream`; calls return before it
+ *    completes and never synchronise or copy device->host. Host-known bounds
+ *    (max_context_len, max_seqlen_q/k) are arguments for that reason.
+ *  - Errors: every call checks its host-visible arguments before enqueuing
+ *    anything and returns a pa_status; nothing throws or aborts. A failed
+ *    launch returns PA_ERR_HIP and pa_last_hip_error() gives the HIP text.
+ *    Device-side contents (table entries, slots, lengths) are not validated:
+ *    an out-of-range block id read through a table, a slot_mapping with
+ *    duplicate slots, or lengths above the stated bounds are undefined
+ *    behaviour, except where a call below says otherwise.
+ *  - Element types: "bf16" is bfloat16 (2 bytes); "fp8" is OCP FP8 E4M3 with
+ *    no infinities (bias 7, largest finite 448, 0x7F/0xFF NaN).
+ *
+ * KV pool layout (one pool for K, one for V, per layer), x = 16 / element size
+ * (8 for bf16, 16 for fp8), token slot s -> block s / block_size, offset
+ * o = s % block_size:
+ *   K [num_blocks][num_kv_heads][head_dim/x][block_size][x]
+ *     element (b, h, o, d) at ((((b*Hkv + h)*(D/x) + d/x)*block_size + o)*x + d%x
+ *   V [num_blocks][num_kv_heads][block_size/x][head_dim][x]
+ *     element (b, h, o, d) at ((((b*Hkv + h)*(block_size/x) + o/x)*D + d)*x + o%x
+ * Each (block, head) slab of block_size*head_dim elements is contiguous. K
+ * keeps x consecutive head-dim values of one token in 16 bytes; V keeps x
+ * consecutive tokens of one head-dim index in 16 bytes.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = -2,       /* sizes are negative or inconsistent                   */
+  PA_ERR_UNSUPPORTED = -3, /* head_dim, block_size, group size or dtype not built  */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required           */
+  PA_ERR_HIP = -5          /* a HIP call failed; see pa_last_hip_error()            */
+} pa_status;
+
+typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+
+/* One layer's pool. Supported: block_size in {16,32,64,128,256}, head_dim in
+ * {64,128}. For PA_KV_FP8_E4M3, k_scale/v_scale are device float32 arrays of
+ * num_kv_heads dequantisation scales (stored byte b means value(b) * scale[h]);
+ * both are ignored (may be NULL) for PA_KV_BF16. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_kv_dtype dtype;
+  const float* k_scale;
+  const float* v_scale;
+} pa_cache_desc;
+
+/* pa_store_kv — write new tokens' keys and values into their cache slots.
+ * The slot mapping is the per-token result of the block manager's allocation
+ * (blocks hold a fixed number of tokens: "Nano-vLLM…", 三.1, 块管理器).
+ *   k, v          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous
+ *   slot_mapping  device int32 [num_tokens]; token t goes to slot slot_mapping[t];
+ *                 a slot < 0 or >= num_blocks*block_size is skipped (padding)
+ *   k_cache, v_cache  device pools in the layout above
+ * bf16 pools receive the bf16 bits unchanged. fp8 pools receive the E4M3 code
+ * nearest to the float32 quotient value/scale[h] (IEEE correctly-rounded
+ * division), ties to even, magnitudes beyond 448 saturated to 448.
+ * Only the addressed slots are written. Duplicate slots: one of the writers wins.
+ * num_tokens == 0 is a no-op. */
+pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache,
+                      const pa_cache_desc* cache, hipStream_t stream);
+
+/* Bytes of device workspace pa_decode needs for these bounds (0 when no
+ * sequence can span more than one partition). partition_size as in pa_decode. */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/* Partition size pa_decode uses for these bounds (resolves 0 = automatic). */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* pa_decode — one query token per sequence attends to its sequence's cached
+ * keys/values through its block table (PagedAttention, "DeepSeek复刻vLLM…",
+ * section vLLM：大模型推理的加速引擎与挑战).
+ *   q             device bf16 [num_seqs][num_q_heads][head_dim]
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at or past
+ *                 ceil(context_lens[s]/block_size) are never read
+ *   context_lens  device int32 [num_seqs]; sequence s attends to logical
+ *                 positions 0..context_lens[s]-1 (its newest token included);
+ *                 0 gives a zero output row; values are clamped to
+ *                 min(max_context_len, max_blocks_per_seq*block_size)
+ *   max_context_len  host bound >= every context_lens[s]; sizes the grid
+ *   scale         softmax scale (e.g. 1/sqrt(head_dim))
+ *   out           device bf16 [num_seqs][num_q_heads][head_dim], fully written
+ *   partition_size   0 = automatic, else a multiple of 256 tokens: contexts
+ *                 longer than one partition are split and merged by a
+ *                 log-sum-exp reduce
+ *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0); contents on entry ignored
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads); the group size
+ * num_q_heads / num_kv_heads must be 1, 2, 4 or 8. Output: softmax(scale*q.k)
+ * weighted sum of v, float32 accumulation, rounded to nearest-even bf16. */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, void* out,
+                    const pa_cache_desc* cache, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* pa_prefill_varlen — causal attention of packed query chunks over their
+ * sequences' paged keys (cached prefix plus the chunk itself, already written by
+ * pa_store_kv): chunked prefill ("nano-vllm-lite…", 核心技术改进 §2).
+ *   q             device bf16 [total_q][num_q_heads][head_dim]; sequence s owns
+ *                 rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
+ *   k_cache, v_cache  the paged pools (bf16 only; fp8 pools return
+ *                 PA_ERR_UNSUPPORTED)
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs+1] prefix sums; sequence s
+ *                 has Lq = cu_q[s+1]-cu_q[s] queries and Lk = cu_k[s+1]-cu_k[s]
+ *                 keys at logical positions 0..Lk-1 of its block table
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   max_seqlen_q, max_seqlen_k  host bounds >= every Lq, Lk; Lq is clamped to
+ *                 max_seqlen_q and Lk to min(max_seqlen_k, max_blocks_per_seq*block_size)
+ *   out           device bf16 [total_q][num_q_heads][head_dim]
+ * Query i of sequence s sits at position Lk-Lq+i and attends to keys 0..Lk-Lq+i
+ * (mask aligned bottom-right); a row that sees no key is written as zeros. */
+pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, float scale, void* out,
+                            const pa_cache_desc* cache, hipStream_t stream);
+
+/* Static text for a status code; never NULL. */
+const char* pa_status_string(pa_status s);
+
+/* Text of the last HIP error seen by a pa_* call on this thread ("" if none). */
+const char* pa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,225 @@
+"""Python binding of libpa, the paged KV-cache attention library for MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/pa.h``. torch provides device memory and the stream.
+The first call loads ``libpa.so`` and raises if it is missing; there is no
+fallback implementation.
+
+Pools are torch tensors in the library's layout (x = 8 for bf16, 16 for fp8):
+    K: (num_blocks, num_kv_heads, head_dim // x, block_size, x)
+    V: (num_blocks, num_kv_heads, block_size // x, head_dim, x)
+bf16 pools have dtype torch.bfloat16, fp8 (E4M3) pools torch.uint8.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = ["store_kv", "decode", "prefill_varlen", "decode_workspace_size",
+           "decode_partition_size", "empty_pools", "PaError", "LIB_PATH", "library"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        lib = library()
+        msg = lib.pa_status_string(status).decode()
+        if status == -5:
+            msg += ": " + lib.pa_last_hip_error().decode()
+        super().__init__(f"{where}: status {status}: {msg}")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m paged_kv_cache_store_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    D = ctypes.POINTER(CacheDesc)
+    lib.pa_store_kv.argtypes = [P, P, P, I32, P, P, D, P]
+    lib.pa_decode_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.pa_decode_workspace_size.restype = SZ
+    lib.pa_decode_partition_size.argtypes = [I32, I32, I32, I32]
+    lib.pa_decode_partition_size.restype = I32
+    lib.pa_decode.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
+    lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
+    for name in ("pa_store_kv", "pa_decode", "pa_prefill_varlen"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_hip_error.argtypes = []
+    lib.pa_last_hip_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = None
+
+
+def library():
+    """The loaded ctypes library; loads it on first use and raises if it is not built."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _pool_desc(k_cache, v_cache, k_scale, v_scale):
+    if k_cache.dtype == torch.bfloat16:
+        dtype, x = PA_KV_BF16, 8
+    elif k_cache.dtype == torch.uint8:
+        dtype, x = PA_KV_FP8_E4M3, 16
+    else:
+        raise ValueError(f"k_cache dtype {k_cache.dtype} is neither bfloat16 nor uint8 (fp8)")
+    _check(k_cache, "k_cache", k_cache.dtype, 5)
+    _check(v_cache, "v_cache", k_cache.dtype, 5, k_cache.device)
+    nb, hkv, dx, bs, xx = k_cache.shape
+    if xx != x or tuple(v_cache.shape) != (nb, hkv, bs // x, dx * x, x) or bs % x:
+        raise ValueError(f"pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} "
+                         f"do not match the layout for x={x}")
+    if dtype == PA_KV_FP8_E4M3:
+        for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+            if sc is None:
+                raise ValueError(f"{name} is required for an fp8 pool")
+            _check(sc, name, torch.float32, 1, k_cache.device)
+            if sc.numel() != hkv:
+                raise ValueError(f"{name} must have num_kv_heads={hkv} entries")
+    desc = CacheDesc(nb, bs, hkv, dx * x, dtype,
+                     k_scale.data_ptr() if dtype == PA_KV_FP8_E4M3 else None,
+                     v_scale.data_ptr() if dtype == PA_KV_FP8_E4M3 else None)
+    return desc, nb, hkv, dx * x, bs
+
+
+def empty_pools(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype="bf16", device="cuda"):
+    """Uninitialised K and V pools in the library's layout."""
+    if kv_dtype == "fp8":
+        x, dt = 16, torch.uint8
+    elif kv_dtype == "bf16":
+        x, dt = 8, torch.bfloat16
+    else:
+        raise ValueError(kv_dtype)
+    k = torch.empty((num_blocks, num_kv_heads, head_dim // x, block_size, x), dtype=dt, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, block_size // x, head_dim, x), dtype=dt, device=device)
+    return k, v
+
+
+def store_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None):
+    """Write k, v ([T, Hkv, D] bf16) into the pools at slot_mapping ([T] int32; <0 skips)."""
+    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
+    dev = k_cache.device
+    _check(k, "k", torch.bfloat16, 3, dev)
+    _check(v, "v", torch.bfloat16, 3, dev)
+    _check(slot_mapping, "slot_mapping", torch.int32, 1, dev)
+    T = k.shape[0]
+    if tuple(k.shape) != (T, hkv, d) or tuple(v.shape) != (T, hkv, d) or slot_mapping.numel() != T:
+        raise ValueError("k, v must be [T, num_kv_heads, head_dim] and slot_mapping [T]")
+    st = library().pa_store_kv(_ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache),
+                          ctypes.byref(desc), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_store_kv")
+
+
+def decode_partition_size(num_seqs, num_q_heads, max_context_len, partition_size=0):
+    return int(library().pa_decode_partition_size(num_seqs, num_q_heads, max_context_len, partition_size))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size=0):
+    return int(library().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                             partition_size))
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
+           k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None):
+    """Paged decode attention; returns out ([S, Hq, D] bf16)."""
+    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
+    dev = k_cache.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    _check(context_lens, "context_lens", torch.int32, 1, dev)
+    S, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != S or context_lens.numel() != S:
+        raise ValueError("q [S, Hq, D], block_tables [S, MB] and context_lens [S] disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    mb = block_tables.shape[1]
+    cap = min(int(max_context_len), mb * bs)
+    need = decode_workspace_size(S, hq, d, cap, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), mb,
+                        _ptr(context_lens), S, hq, int(max_context_len), float(scale), _ptr(out),
+                        ctypes.byref(desc), int(partition_size), _ptr(workspace), wbytes,
+                        _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_decode")
+    return out
+
+
+def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, scale,
+                   max_seqlen_q, max_seqlen_k, out=None, stream=None):
+    """Causal varlen prefill over the paged pools; returns out ([Tq, Hq, D] bf16)."""
+    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, None, None)
+    dev = k_cache.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    S = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != S + 1 or block_tables.shape[0] != S or q.shape[2] != d:
+        raise ValueError("cu_seqlens_q/k [S+1], block_tables [S, MB] and q [Tq, Hq, D] disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    st = library().pa_prefill_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
+                                _ptr(cu_seqlens_k), _ptr(block_tables), block_tables.shape[1], S,
+                                q.shape[1], int(max_seqlen_q), int(max_seqlen_k), float(scale),
+                                _ptr(out), ctypes.byref(desc), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_prefill_varlen")
+    return out
+
+
+def header_functions(header_path=None):
+    """Names of the functions include/pa.h declares."""
+    path = header_path or os.path.join(os.path.dirname(os.path.dirname(LIB_PATH)), "include", "pa.h")
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))

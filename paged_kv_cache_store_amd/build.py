@@ -1,0 +1,64 @@
+"""Build libpa.so (gfx950) in-tree with hipcc.
+
+    python -m paged_kv_cache_store_amd.build
+
+Every HIP source under csrc/ is compiled for gfx950 only and linked into
+paged_kv_cache_store_amd/libpa.so next to this file. Flags:
+* -O3, -fPIC, --offload-arch=gfx950;
+* packed-fp32 instructions disabled (-target-feature -packed-fp32-ops);
+* IEEE-correct float32 division kept explicit
+  (-fhip-fp32-correctly-rounded-divide-sqrt): the fp8 store depends on it.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libpa.so")
+SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+DEVICE_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("build step failed: " + " ".join(cmd))
+    # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
+    noise = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and "packed-fp32-ops" not in ln]
+    if noise:
+        sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpa.so; returns the library path."""
+    with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            cmd = [HIPCC, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd))
+            _run(cmd)
+            objs.append(obj)
+        out_tmp = os.path.join(tmp, "libpa.so")
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp])
+        shutil.move(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,164 @@
+// C ABI of libpa (declared in include/pa.h): argument checks, then launches.
+// Every check below runs on the host before anything is enqueued, so a bad
+// argument never reaches the GPU and the checks can be exercised without one.
+#include <stdio.h>
+#include <string.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+pa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return PA_ERR_HIP;
+}
+
+bool supported_block_size(int bs) {
+  return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
+}
+
+pa_status check_cache(const pa_cache_desc* c, pa::PoolDims* dims) {
+  if (!c) return PA_ERR_NULL;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (!supported_block_size(c->block_size)) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+  if (c->dtype == PA_KV_FP8_E4M3 && (!c->k_scale || !c->v_scale)) return PA_ERR_NULL;
+  dims->num_blocks = c->num_blocks;
+  dims->block_size = c->block_size;
+  dims->num_kv_heads = c->num_kv_heads;
+  dims->head_dim = c->head_dim;
+  dims->fp8 = c->dtype == PA_KV_FP8_E4M3;
+  return PA_OK;
+}
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
+// Automatic partition size: about four partitions for the longest context,
+// between 256 and 1024 tokens.
+int32_t auto_partition(int32_t max_context_len) {
+  int32_t p = round_up((max_context_len + 3) / 4, 256);
+  if (p < 256) p = 256;
+  if (p > 1024) p = 1024;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "sizes are negative or inconsistent";
+    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or dtype not supported";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP error (see pa_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_hip_error(void) { return g_hip_error; }
+
+pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_cache, void* v_cache,
+                      const pa_cache_desc* cache, hipStream_t stream) {
+  pa::PoolDims dims;
+  pa_status st = check_cache(cache, &dims);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+  return hip_status(pa::launch_store_kv(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                        slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
+                                        static_cast<uint8_t*>(v_cache), dims, cache->k_scale,
+                                        cache->v_scale, stream));
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_size) {
+  (void)num_seqs;
+  (void)num_q_heads;
+  if (partition_size > 0) return partition_size;
+  return auto_partition(max_context_len < 0 ? 0 : max_context_len);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, max_context_len, partition_size);
+  if (P <= 0) return 0;
+  const int32_t np = (max_context_len + P - 1) / P;
+  return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
+}
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, void* out,
+                    const pa_cache_desc* cache, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pa::PoolDims dims;
+  pa_status st = check_cache(cache, &dims);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % dims.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!supported_group(num_q_heads / dims.num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % 256 != 0) return PA_ERR_SHAPE;
+  if (!(scale == scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  // the grid covers contexts up to the smaller of the two host bounds
+  const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
+  const int32_t cap = int32_t(cap_ll < max_context_len ? cap_ll : max_context_len);
+  const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, cap, partition_size);
+  if (P / dims.block_size > 256) return PA_ERR_UNSUPPORTED;  // block ids of a partition live in LDS
+  const int32_t np = cap > 0 ? (cap + P - 1) / P : 1;
+  const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, dims.head_dim, np);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  return hip_status(pa::launch_decode(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
+                                      static_cast<const uint8_t*>(v_cache), block_tables,
+                                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, cap,
+                                      scale, static_cast<uint16_t*>(out), dims, cache->k_scale,
+                                      cache->v_scale, P, workspace, stream));
+}
+
+pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, float scale, void* out,
+                            const pa_cache_desc* cache, hipStream_t stream) {
+  pa::PoolDims dims;
+  pa_status st = check_cache(cache, &dims);
+  if (st != PA_OK) return st;
+  if (dims.fp8) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % dims.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (!supported_group(num_q_heads / dims.num_kv_heads)) return PA_ERR_UNSUPPORTED;
+  if (!(scale == scale)) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
+    return PA_ERR_NULL;
+  const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
+  const int32_t cap_k = int32_t(cap_ll < max_seqlen_k ? cap_ll : max_seqlen_k);
+  return hip_status(pa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
+                                       static_cast<const uint8_t*>(v_cache), cu_seqlens_q, cu_seqlens_k,
+                                       block_tables, max_blocks_per_seq, num_seqs, num_q_heads,
+                                       max_seqlen_q, cap_k, scale, static_cast<uint16_t*>(out), dims,
+                                       stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// Paged decode attention (one query token per sequence) and the log-sum-exp
+// reduce that merges context partitions.
+//
+// PagedAttention reads a sequence's keys/values from non-contiguous fixed-size
+// blocks through its block table ("DeepSeek复刻vLLM反超原版：AI推理新标杆", section
+// vLLM：大模型推理的加速引擎与挑战); decode is bound by the bandwidth of these
+// KV-cache reads ("nano-vllm-lite：深入理解LLM推理机制的教育级开源项目", 核心技术改进
+// §2), and the KV may be stored as FP8 (same page, §3). The attention itself is
+// exact softmax(scale * q.k) v, computed the memory-efficient way with a running
+// maximum and sum ("Nano-vLLM：轻量高效的大模型推理框架…", 三.3 模型层适配).
+//
+// Work decomposition (CDNA4, wave64):
+// * one workgroup of 4 waves per (sequence, KV head, context partition); it
+//   serves all G query heads of the KV head, so every K/V byte is read once;
+// * a wave takes 64-key tiles of the partition in turn (tile t -> wave t % 4);
+// * QK: lane = key. The K layout keeps 8 (bf16) or 16 (fp8) head-dim values of
+//   one key in 16 bytes and consecutive keys in consecutive 16-byte slots, so a
+//   wave's load of chunk c covers 1 KiB contiguous; the lane forms the whole dot
+//   product for its key with v_dot2_f32_bf16 against wave-uniform query pairs,
+//   with no cross-lane reduction;
+// * softmax: per tile, a DPP wave maximum per query head, running max/sum with
+//   rescaling (base-2 exponentials, log2(e) folded into the scale);
+// * PV: lane = head-dim index. The V layout keeps 8 (bf16) or 16 (fp8)
+//   consecutive keys of one head-dim index in 16 bytes, so a lane dots its V
+//   chunk with the chunk's bf16 weights (broadcast from LDS) via v_dot2;
+// * the 4 waves' partial (max, sum, output) are merged in LDS; a sequence that
+//   fits one partition writes its bf16 output, a longer one writes an
+//   unnormalised float32 partial for the reduce kernel.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kDecodeWaves = kDecodeThreads / kWave;
+constexpr int kTile = 64;            // keys per wave per step
+constexpr int kMaxPartBlocks = 256;  // block ids per partition staged in LDS
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  uint16_t* out;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int max_blocks_per_seq;
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int part_size;   // P, multiple of 256
+  int num_parts;   // NP = ceil(context cap / P)
+  int ctx_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
+  float scale_log2;
+};
+
+template <int kD, int kG, bool kFp8>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
+  constexpr int kX = kFp8 ? 16 : 8;       // elements per 16-byte chunk
+  constexpr int kKC = kD / kX;            // K chunks per key
+  constexpr int kVC = kTile / kX;         // V key-chunks per tile
+  constexpr int kDL = kD / kWave;         // head-dim values per lane in PV
+  constexpr int kQW = kD / 2;             // query dwords (bf16 pairs) per head
+  constexpr int kPW = kX / 2;             // weight dwords per V key-chunk
+
+  __shared__ int blk_s[kMaxPartBlocks];
+  __shared__ __attribute__((aligned(16))) uint16_t p_s[kDecodeWaves][kG][kTile];
+  __shared__ float m_s[kDecodeWaves][kG];
+  __shared__ float l_s[kDecodeWaves][kG];
+  __shared__ float o_s[kDecodeWaves][kG][kD];
+
+  const int Hkv = a.num_kv_heads;
+  const int bid = blockIdx.x;
+  const int h = bid % Hkv;  // KV head varies fastest: consecutive workgroups go to different XCDs
+  const int rest = bid / Hkv;
+  const int part = rest % a.num_parts;
+  const int s = rest / a.num_parts;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, uniform
+  const int lane = tid % kWave;
+  const int bs = a.block_size;
+  const int P = a.part_size;
+
+  int n = a.context_lens[s];
+  n = n < a.ctx_cap ? n : a.ctx_cap;
+  const int p0 = part * P;
+  if (n <= 0) {
+    if (part == 0) {
+      for (int i = tid; i < kG * kD; i += kDecodeThreads)
+        a.out[((long long)s * a.num_q_heads + h * kG) * kD + i] = 0;
+    }
+    return;
+  }
+  if (p0 >= n) return;
+  const int pend = min(p0 + P, n);
+  const int nsplit = (n + P - 1) / P;
+
+  // physical block ids of this partition
+  const int nb = (pend - p0 + bs - 1) / bs;
+  const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq + p0 / bs;
+  for (int i = tid; i < nb; i += kDecodeThreads) blk_s[i] = bt[i];
+  __syncthreads();
+
+  const uint32_t* qg =
+      reinterpret_cast<const uint32_t*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD);
+  const float sc = kFp8 ? a.scale_log2 * a.k_scale[h] : a.scale_log2;
+  const long long slab16 = (long long)bs * kD * (kFp8 ? 1 : 2) / 16;  // 16-byte units per (block, head)
+  const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache) + (long long)h * slab16;
+  const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache) + (long long)h * slab16;
+  const long long blk_stride16 = (long long)Hkv * slab16;
+
+  float m[kG], l[kG], acc[kG][kDL];
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kDL; ++j) acc[g][j] = 0.f;
+  }
+
+  const int ntiles = (pend - p0 + kTile - 1) / kTile;
+  for (int t = w; t < ntiles; t += kDecodeWaves) {
+    const int key0 = p0 + t * kTile;
+    const int key = key0 + lane;
+    const bool valid = key < pend;
+    // ---- issue all loads of the tile: K (lane = key), V (lane = head-dim index)
+    uint4 kr[kKC];
+    {
+      const int rel = (valid ? key : pend - 1) - p0;
+      const uint4* kp = kbase + blk_s[rel / bs] * blk_stride16 + (rel % bs);
+#pragma unroll
+      for (int c = 0; c < kKC; ++c) kr[c] = kp[(long long)c * bs];
+    }
+    uint4 vr[kVC][kDL];
+#pragma unroll
+    for (int j = 0; j < kVC; ++j) {
+      int kk = key0 + j * kX;
+      if (kk >= pend) kk = (pend - 1) & ~(kX - 1);  // stay inside written blocks; result unused
+      const int rel = kk - p0;
+      const uint4* vp = vbase + blk_s[rel / bs] * blk_stride16 + (long long)((rel % bs) / kX) * kD;
+#pragma unroll
+      for (int dl = 0; dl < kDL; ++dl) vr[j][dl] = vp[lane + dl * kWave];
+    }
+    // ---- scores
+    float sv[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) sv[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kKC; ++c) {
+      const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (!kFp8) {
+#pragma unroll
+          for (int g = 0; g < kG; ++g) sv[g] = dot2_bf16(kw[i], qg[g * kQW + c * 4 + i], sv[g]);
+        } else {
+          const uint32_t lo = fp8x2_to_bf16x2<false>(kw[i]);
+          const uint32_t hi = fp8x2_to_bf16x2<true>(kw[i]);
+#pragma unroll
+          for (int g = 0; g < kG; ++g) {
+            sv[g] = dot2_bf16(lo, qg[g * kQW + c * 8 + 2 * i], sv[g]);
+            sv[g] = dot2_bf16(hi, qg[g * kQW + c * 8 + 2 * i + 1], sv[g]);
+          }
+        }
+      }
+    }
+    // ---- online softmax (base 2)
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const float x = valid ? sv[g] * sc : -INFINITY;
+      const float mn = fmaxf(m[g], wave_max(x));
+      const float alpha = fast_exp2(m[g] - mn);
+      const uint32_t pb = f32_to_bf16(fast_exp2(x - mn));
+      l[g] = l[g] * alpha + bf16_lo(pb);
+#pragma unroll
+      for (int dl = 0; dl < kDL; ++dl) acc[g][dl] *= alpha;
+      m[g] = mn;
+      p_s[w][g][lane] = uint16_t(pb);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- PV
+#pragma unroll
+    for (int j = 0; j < kVC; ++j) {
+      const int kk = key0 + j * kX;
+      if (kk >= pend) break;
+      const int nv = pend - kk;
+      uint32_t pw[kG][kPW];
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const uint4* pp = reinterpret_cast<const uint4*>(&p_s[w][g][j * kX]);
+#pragma unroll
+        for (int u = 0; u < kPW / 4; ++u) {
+          const uint4 t4 = pp[u];
+          pw[g][4 * u + 0] = t4.x;
+          pw[g][4 * u + 1] = t4.y;
+          pw[g][4 * u + 2] = t4.z;
+          pw[g][4 * u + 3] = t4.w;
+        }
+      }
+#pragma unroll
+      for (int dl = 0; dl < kDL; ++dl) {
+        uint32_t vw[4] = {vr[j][dl].x, vr[j][dl].y, vr[j][dl].z, vr[j][dl].w};
+        if (nv < kX) {  // last chunk of the context: zero the values past its end
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t mask = 0;
+            if constexpr (!kFp8) {
+              mask = (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+            } else {
+#pragma unroll
+              for (int b = 0; b < 4; ++b) mask |= (4 * i + b < nv) ? (0xffu << (8 * b)) : 0u;
+            }
+            vw[i] &= mask;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (!kFp8) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) acc[g][dl] = dot2_bf16(vw[i], pw[g][i], acc[g][dl]);
+          } else {
+            const uint32_t lo = fp8x2_to_bf16x2<false>(vw[i]);
+            const uint32_t hi = fp8x2_to_bf16x2<true>(vw[i]);
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+              acc[g][dl] = dot2_bf16(lo, pw[g][2 * i], acc[g][dl]);
+              acc[g][dl] = dot2_bf16(hi, pw[g][2 * i + 1], acc[g][dl]);
+            }
+          }
+        }
+      }
+    }
+    // the next tile's weights overwrite p_s: finish this tile's reads first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the 4 waves
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const float lw = wave_sum(l[g]);
+    if (lane == 0) {
+      m_s[w][g] = m[g];
+      l_s[w][g] = lw;
+    }
+#pragma unroll
+    for (int dl = 0; dl < kDL; ++dl) o_s[w][g][lane + dl * kWave] = acc[g][dl];
+  }
+  __syncthreads();
+  const float vsc = kFp8 ? a.v_scale[h] : 1.f;
+  for (int i = tid; i < kG * kD; i += kDecodeThreads) {
+    const int g = i / kD;
+    const int d = i % kD;
+    float M = m_s[0][g];
+#pragma unroll
+    for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, m_s[ww][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecodeWaves; ++ww) {
+      const float e = fast_exp2(m_s[ww][g] - M);
+      L += l_s[ww][g] * e;
+      O += o_s[ww][g][d] * e;
+    }
+    const long long row = (long long)s * a.num_q_heads + h * kG + g;
+    if (nsplit == 1) {
+      a.out[row * kD + d] = uint16_t(f32_to_bf16(O / L * vsc));
+    } else {
+      const long long pr = row * a.num_parts + part;
+      a.part_o[pr * kD + d] = O * vsc;
+      if (d == 0) {
+        a.part_m[pr] = M;
+        a.part_l[pr] = L;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of a sequence's partitions: with per-partition maxima m_p
+// (log2 units), weight sums l_p and unnormalised outputs o_p,
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One wave per (sequence, query head); sequences with one partition were
+// finished by the decode kernel.
+template <int kD>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(
+    const int32_t* __restrict__ context_lens, int ctx_cap, int part_size, int num_parts,
+    int num_q_heads, const float* __restrict__ part_o, const float* __restrict__ part_m,
+    const float* __restrict__ part_l, uint16_t* __restrict__ out) {
+  constexpr int kDL = kD / kWave;
+  const int s = blockIdx.x / num_q_heads;
+  const int hq = blockIdx.x % num_q_heads;
+  int n = context_lens[s];
+  n = n < ctx_cap ? n : ctx_cap;
+  const int nsplit = (n + part_size - 1) / part_size;
+  if (nsplit <= 1) return;
+  const long long base = ((long long)s * num_q_heads + hq) * num_parts;
+  float M = -INFINITY;
+  for (int p = 0; p < nsplit; ++p) M = fmaxf(M, part_m[base + p]);
+  float L = 0.f, O[kDL];
+#pragma unroll
+  for (int dl = 0; dl < kDL; ++dl) O[dl] = 0.f;
+  for (int p = 0; p < nsplit; ++p) {
+    const float e = fast_exp2(part_m[base + p] - M);
+    L += part_l[base + p] * e;
+#pragma unroll
+    for (int dl = 0; dl < kDL; ++dl) O[dl] += part_o[(base + p) * kD + threadIdx.x + dl * kWave] * e;
+  }
+  const long long row = (long long)s * num_q_heads + hq;
+#pragma unroll
+  for (int dl = 0; dl < kDL; ++dl)
+    out[row * kD + threadIdx.x + dl * kWave] = uint16_t(f32_to_bf16(O[dl] / L));
+}
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts) {
+  if (num_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * num_parts;
+  return rows * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+template <int kD, int kG, bool kFp8>
+static void launch_decode_t(const DecodeArgs& a, unsigned grid, hipStream_t stream) {
+  decode_kernel<kD, kG, kFp8><<<grid, kDecodeThreads, 0, stream>>>(a);
+}
+
+template <int kD, bool kFp8>
+static bool launch_decode_g(int G, const DecodeArgs& a, unsigned grid, hipStream_t stream) {
+  switch (G) {
+    case 1: launch_decode_t<kD, 1, kFp8>(a, grid, stream); return true;
+    case 2: launch_decode_t<kD, 2, kFp8>(a, grid, stream); return true;
+    case 4: launch_decode_t<kD, 4, kFp8>(a, grid, stream); return true;
+    case 8: launch_decode_t<kD, 8, kFp8>(a, grid, stream); return true;
+    default: return false;
+  }
+}
+
+hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                         int max_context_len, float scale, uint16_t* out, const PoolDims& pool,
+                         const float* k_scale, const float* v_scale, int partition_size,
+                         void* workspace, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  const int D = pool.head_dim;
+  const int G = num_q_heads / pool.num_kv_heads;
+  const long long cap_ll = (long long)max_blocks_per_seq * pool.block_size;
+  const int ctx_cap = int(cap_ll < max_context_len ? cap_ll : max_context_len);
+  const int P = partition_size;
+  const int NP = ctx_cap > 0 ? (ctx_cap + P - 1) / P : 1;
+  DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.out = out;
+  const size_t rows = (size_t)num_seqs * num_q_heads * NP;
+  float* ws = static_cast<float*>(workspace);
+  a.part_o = NP > 1 ? ws : nullptr;
+  a.part_m = NP > 1 ? ws + rows * D : nullptr;
+  a.part_l = NP > 1 ? ws + rows * (D + 1) : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool.num_kv_heads;
+  a.block_size = pool.block_size;
+  a.part_size = P;
+  a.num_parts = NP;
+  a.ctx_cap = ctx_cap;
+  a.scale_log2 = scale * kLog2e;
+  const unsigned grid = unsigned((long long)num_seqs * pool.num_kv_heads * NP);
+  bool ok;
+  if (D == 64)
+    ok = pool.fp8 ? launch_decode_g<64, true>(G, a, grid, stream)
+                  : launch_decode_g<64, false>(G, a, grid, stream);
+  else
+    ok = pool.fp8 ? launch_decode_g<128, true>(G, a, grid, stream)
+                  : launch_decode_g<128, false>(G, a, grid, stream);
+  if (!ok) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || NP <= 1) return e;
+  const unsigned rgrid = unsigned((long long)num_seqs * num_q_heads);
+  if (D == 64)
+    decode_reduce_kernel<64><<<rgrid, kWave, 0, stream>>>(context_lens, ctx_cap, P, NP, num_q_heads,
+                                                          a.part_o, a.part_m, a.part_l, out);
+  else
+    decode_reduce_kernel<128><<<rgrid, kWave, 0, stream>>>(context_lens, ctx_cap, P, NP, num_q_heads,
+                                                           a.part_o, a.part_m, a.part_l, out);
+  return hipGetLastError();
+}
+
+}  // namespace pa

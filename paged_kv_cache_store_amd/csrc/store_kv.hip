@@ -1,0 +1,97 @@
+// KV store: scatter new tokens' K/V rows into their block-pool slots.
+//
+// A slot names a fixed-size block and an offset inside it (blocks hold the KV
+// of a fixed number of tokens: "Nano-vLLM：轻量高效的大模型推理框架…", 三.1 推理引擎架构,
+// 块管理器). Optional FP8 E4M3 storage halves the pool ("nano-vllm-lite：深入理解
+// LLM推理机制的教育级开源项目", 核心技术改进 §3).
+//
+// One thread moves one 16-byte chunk of the pool's K layout: 8 bf16 head-dim
+// values of one (token, head) for a bf16 pool, 16 values (read as 32 bytes of
+// bf16 input) for an fp8 pool. K chunks are written whole; V is transposed in
+// the pool (x consecutive tokens per 16 bytes), so each value lands in its own
+// 2-byte (bf16) or 1-byte (fp8) position. Reads of k/v are fully coalesced.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+template <bool kFp8>
+__global__ __launch_bounds__(256) void store_kv_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ slots, int num_tokens, int num_kv_heads, int head_dim,
+    int block_size, long long num_slots, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  constexpr int kX = kFp8 ? 16 : 8;  // elements per 16-byte pool chunk
+  const int chunks = head_dim / kX;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)num_tokens * num_kv_heads * chunks;
+  if (idx >= total) return;
+  const int c = int(idx % chunks);
+  const long long th = idx / chunks;
+  const int h = int(th % num_kv_heads);
+  const long long t = th / num_kv_heads;
+  const long long slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const long long b = slot / block_size;
+  const int o = int(slot % block_size);
+  const long long slab = (b * num_kv_heads + h) * (long long)block_size * head_dim;  // elements
+  const long long src = (t * num_kv_heads + h) * head_dim + (long long)c * kX;
+  // K: chunk c of this token at [b][h][c][o][:]
+  const long long k_dst = slab + ((long long)c * block_size + o) * kX;
+  // V: value d at [b][h][o / x][d][o % x]
+  const long long v_dst = slab + (long long)(o / kX) * head_dim * kX + (o % kX);
+  if constexpr (!kFp8) {
+    const uint4 kr = *reinterpret_cast<const uint4*>(k + src);
+    const uint4 vr = *reinterpret_cast<const uint4*>(v + src);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + k_dst) = kr;
+    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache) + v_dst + (long long)c * kX * kX;
+    const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      vc[e * kX] = uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+  } else {
+    const float ks = k_scale[h];
+    const float vs = v_scale[h];
+    const uint4* kp = reinterpret_cast<const uint4*>(k + src);
+    const uint4* vp = reinterpret_cast<const uint4*>(v + src);
+    const uint4 ka = kp[0], kb = kp[1], va = vp[0], vb = vp[1];
+    const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    const uint32_t vw[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+    uint32_t kout[4] = {0u, 0u, 0u, 0u};
+    uint8_t* vc = v_cache + v_dst + (long long)c * kX * kX;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t kbits = (e & 1) ? (kw[e >> 1] & 0xffff0000u) : (kw[e >> 1] << 16);
+      const uint32_t vbits = (e & 1) ? (vw[e >> 1] & 0xffff0000u) : (vw[e >> 1] << 16);
+      // correctly rounded float32 division (HIP's default for '/')
+      const uint32_t kcode = e4m3_encode(__uint_as_float(kbits) / ks);
+      const uint32_t vcode = e4m3_encode(__uint_as_float(vbits) / vs);
+      kout[e >> 2] |= kcode << (8 * (e & 3));
+      vc[e * kX] = uint8_t(vcode);
+    }
+    *reinterpret_cast<uint4*>(k_cache + k_dst) = make_uint4(kout[0], kout[1], kout[2], kout[3]);
+  }
+}
+
+hipError_t launch_store_kv(const uint16_t* k, const uint16_t* v, const int32_t* slots,
+                           int num_tokens, uint8_t* k_cache, uint8_t* v_cache,
+                           const PoolDims& pool, const float* k_scale, const float* v_scale,
+                           hipStream_t stream) {
+  const int x = pool.fp8 ? 16 : 8;
+  const long long total = (long long)num_tokens * pool.num_kv_heads * (pool.head_dim / x);
+  if (total == 0) return hipSuccess;
+  const unsigned grid = unsigned((total + 255) / 256);
+  const long long num_slots = (long long)pool.num_blocks * pool.block_size;
+  if (pool.fp8)
+    store_kv_kernel<true><<<grid, 256, 0, stream>>>(k, v, slots, num_tokens, pool.num_kv_heads,
+                                                    pool.head_dim, pool.block_size, num_slots,
+                                                    k_cache, v_cache, k_scale, v_scale);
+  else
+    store_kv_kernel<false><<<grid, 256, 0, stream>>>(k, v, slots, num_tokens, pool.num_kv_heads,
+                                                     pool.head_dim, pool.block_size, num_slots,
+                                                     k_cache, v_cache, k_scale, v_scale);
+  return hipGetLastError();
+}
+
+}  // namespace pa

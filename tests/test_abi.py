@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports what include/pa.h declares, and rejects bad
+arguments on the host before any launch (no GPU needed: every call here fails
+validation, so nothing reaches the HIP runtime)."""
+import ctypes
+
+import pytest
+
+pa = pytest.importorskip("paged_kv_cache_store_amd")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def desc(nb=8, bs=16, hkv=2, d=64, dtype=0, ks=None, vs=None):
+    return pa.CacheDesc(nb, bs, hkv, d, dtype, ks, vs)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = pa.header_functions()
+    assert set(names) == {"pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_decode_workspace_size",
+                          "pa_decode_partition_size", "pa_status_string", "pa_last_hip_error"}
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.pa_status_string(s)
+    assert lib.pa_last_hip_error() == b""
+
+
+def store(lib, d, k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE):
+    return lib.pa_store_kv(k, v, slots, T, kc, vc, ctypes.byref(d) if d is not None else None, None)
+
+
+def test_store_validation(lib):
+    assert store(lib, None) == NULL
+    assert store(lib, desc(), k=None) == NULL
+    assert store(lib, desc(), kc=None) == NULL
+    assert store(lib, desc(), T=-1) == SHAPE
+    assert store(lib, desc(), T=0, k=None, v=None, slots=None) == OK      # no-op
+    assert store(lib, desc(bs=48)) == UNSUP
+    assert store(lib, desc(d=96)) == UNSUP
+    assert store(lib, desc(dtype=3)) == UNSUP
+    assert store(lib, desc(nb=0)) == SHAPE
+    assert store(lib, desc(dtype=1)) == NULL                              # fp8 needs scales
+
+
+def decode(lib, d, q=FAKE, S=4, hq=4, maxctx=100, mb=8, P=0, ws=None, wsb=0, scale=0.125):
+    return lib.pa_decode(q, FAKE, FAKE, FAKE, mb, FAKE, S, hq, maxctx, scale, FAKE,
+                         ctypes.byref(d) if d is not None else None, P, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, None) == NULL
+    assert decode(lib, desc(), q=None) == NULL
+    assert decode(lib, desc(), hq=3) == SHAPE                 # Hq % Hkv
+    assert decode(lib, desc(hkv=1), hq=3) == UNSUP            # group 3 not built
+    assert decode(lib, desc(), S=-1) == SHAPE
+    assert decode(lib, desc(), P=100) == SHAPE                # not a multiple of 256
+    assert decode(lib, desc(), scale=float("nan")) == SHAPE
+    assert decode(lib, desc(), S=0, q=None) == OK             # nothing to do
+    # a split decode needs its workspace
+    assert decode(lib, desc(bs=256), maxctx=2048, P=256) == WS
+    need = lib.pa_decode_workspace_size(4, 4, 64, 2048, 256)
+    assert need == 4 * 4 * 8 * (64 + 2) * 4
+    assert decode(lib, desc(bs=256), maxctx=2048, P=256, ws=FAKE, wsb=need - 1) == WS
+    # partition block ids must fit the 256-entry LDS table
+    assert decode(lib, desc(bs=16), maxctx=8192, mb=512, P=8192, ws=FAKE, wsb=1 << 30) == UNSUP
+
+
+def test_workspace_and_partition_rules(lib):
+    assert lib.pa_decode_workspace_size(4, 4, 64, 200, 0) == 0          # one partition: no workspace
+    assert lib.pa_decode_workspace_size(0, 4, 64, 200, 0) == 0
+    assert lib.pa_decode_partition_size(64, 32, 32768, 1024) == 1024
+    for ctx in (1, 100, 1016, 2042, 32657):
+        p = lib.pa_decode_partition_size(1, 1, ctx, 0)
+        assert p % 256 == 0 and 256 <= p <= 1024
+    P = lib.pa_decode_partition_size(64, 32, 32768, 0)
+    assert lib.pa_decode_workspace_size(64, 32, 128, 32768, 0) == 64 * 32 * (32768 // P) * 130 * 4
+
+
+def prefill(lib, d, q=FAKE, S=2, hq=4, mq=16, mk=64, mb=8):
+    return lib.pa_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, FAKE, mb, S, hq, mq, mk, 0.125, FAKE,
+                                 ctypes.byref(d) if d is not None else None, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, None) == NULL
+    assert prefill(lib, desc(), q=None) == NULL
+    assert prefill(lib, desc(), hq=5) == SHAPE
+    assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE)) == UNSUP      # fp8 prefill not built
+    assert prefill(lib, desc(), mq=-1) == SHAPE
+    assert prefill(lib, desc(), S=0, q=None) == OK

@@ -1,0 +1,248 @@
+"""GPU parity of pa_store_kv and pa_decode against the CPU oracle (through the C ABI).
+
+Store: bit-exact (bf16 bits; fp8 codes) over whole pools, NaN sentinels included.
+Decode: element-wise |gpu - oracle| <= atol + rtol*|oracle| with atol = rtol = 1e-2
+for a bf16 cache and 3e-2 for fp8 (oracle on the same fp8 bytes, float64).
+Full-size workloads are checked on sampled sequences the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import GpuCase, host_bits
+from tests.util import assert_close, bf16_f64, oracle_pools, poisoned_pools, relabel_blocks
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (1e-2, 1e-2), "fp8": (3e-2, 3e-2)}
+
+
+def _oracle_decode(w, kc, vc, seqs=None):
+    return oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                   w.block_size, w.k_scale, w.v_scale, seqs=seqs)
+
+
+def _check_pools_equal(case, kc, vc, blocks=None):
+    gk = case.k_cache if blocks is None else case.k_cache[torch.as_tensor(blocks, device="cuda").long()]
+    gv = case.v_cache if blocks is None else case.v_cache[torch.as_tensor(blocks, device="cuda").long()]
+    ok_k = host_bits(gk)
+    ok_v = host_bits(gv)
+    rk = kc if blocks is None else kc[blocks]
+    rv = vc if blocks is None else vc[blocks]
+    nk = np.count_nonzero(ok_k != rk)
+    nv = np.count_nonzero(ok_v != rv)
+    assert nk == 0 and nv == 0, f"pool bytes differ: K {nk}, V {nv}"
+
+
+def _seq_blocks(w, seqs):
+    out = set()
+    for s in seqs:
+        out.update(w.block_tables[s, :math.ceil(int(w.context_lens[s]) / w.block_size)].tolist())
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def _oracle_pools_for(w, seqs):
+    """Oracle pools holding only the tokens of the given sequences' blocks."""
+    blocks = _seq_blocks(w, seqs)
+    kc, vc = poisoned_pools(w) if w.num_blocks <= 2048 else _lazy_pools(w)
+    for slots, k, v in ((w.fill_slots, w.fill_k, w.fill_v), (w.new_slots, w.new_k, w.new_v)):
+        sel = np.isin(slots // w.block_size, blocks)
+        oracle.cache.store(k[sel], v[sel], slots[sel], kc, vc, w.block_size, w.k_scale, w.v_scale)
+    return kc, vc, blocks
+
+
+def _lazy_pools(w):
+    ks, vs = oracle.cache.pool_shapes(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
+    dt = np.uint8 if w.kv_dtype == "fp8" else np.uint16
+    return np.zeros(ks, dt), np.zeros(vs, dt)
+
+
+# ---------------------------------------------------------------- small workloads, whole pools
+EDGE = [
+    dict(seed=101, Hq=4, Hkv=2, D=64, bs=16, context_lens=(0, 1, 15, 16, 17, 63, 64, 65, 200)),
+    dict(seed=102, Hq=8, Hkv=8, D=128, bs=32, context_lens=(1, 31, 32, 33, 300)),
+    dict(seed=103, Hq=16, Hkv=2, D=128, bs=64, context_lens=(5, 127, 128, 129, 700)),
+    dict(seed=104, Hq=16, Hkv=4, D=64, bs=128, context_lens=(255, 256, 257, 1023, 1024, 1025),
+         partition_size=256),
+    dict(seed=105, Hq=32, Hkv=8, D=128, bs=256,
+         context_lens=(1, 255, 256, 257, 511, 512, 513, 1100), partition_size=256),
+    dict(seed=106, Hq=32, Hkv=8, D=128, bs=256, context_lens=(1, 17, 300, 1024, 1025, 3000),
+         kv_dtype="fp8", partition_size=1024),
+    dict(seed=107, Hq=8, Hkv=4, D=64, bs=16, context_lens=(1, 16, 17, 100), kv_dtype="fp8"),
+    dict(seed=108, Hq=8, Hkv=1, D=64, bs=64, context_lens=(2000, 3), kv_dtype="fp8", partition_size=256),
+    dict(seed=109, Hq=4, Hkv=4, D=128, bs=16, context_lens=(4096, 1, 77), partition_size=512),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_store_and_decode_small(cfg):
+    w = W.custom(**cfg)
+    print(f"case {cfg}", flush=True)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    _check_pools_equal(case, kc, vc)
+    for ps in sorted({w.partition_size, 0, 256, 4096}):
+        got = bf16_f64(host_bits(case.decode(partition_size=ps)))
+        ref = _oracle_decode(w, kc, vc)
+        assert_close(got, ref, *TOL[w.kv_dtype], what=f"P={ps}")
+
+
+def test_tiny_decode_workload():
+    w = W.make(1)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    _check_pools_equal(case, kc, vc)
+    got = bf16_f64(host_bits(case.decode()))
+    ma, mr = assert_close(got, _oracle_decode(w, kc, vc), *TOL["bf16"], what="tiny")
+    print(f"[tiny decode] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.fixture(scope="module")
+def qwen3_06b():
+    w = W.make(2)
+    return w, GpuCase(w)
+
+
+def test_qwen3_06b_store_bitexact(qwen3_06b):
+    w, case = qwen3_06b
+    kc, vc = oracle_pools(w)
+    _check_pools_equal(case, kc, vc)
+
+
+def test_qwen3_06b_decode_all_sequences(qwen3_06b):
+    w, case = qwen3_06b
+    kc, vc = oracle_pools(w)
+    got = bf16_f64(host_bits(case.decode()))
+    ma, mr = assert_close(got, _oracle_decode(w, kc, vc), *TOL["bf16"], what="qwen3-0.6b")
+    print(f"[qwen3-0.6b decode] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_qwen3_8b_shared_prefix_sampled():
+    w = W.make(3)
+    case = GpuCase(w)
+    lens = w.context_lens
+    sharers = np.flatnonzero((w.block_tables[:, :2] == w.shared_blocks).all(axis=1))
+    rng = np.random.default_rng(0)
+    seqs = sorted(set([int(lens.argmax()), int(lens.argmin())] + sharers[:6].tolist()
+                      + rng.choice(w.num_seqs, 16, replace=False).tolist()))
+    kc, vc, blocks = _oracle_pools_for(w, seqs)
+    got = bf16_f64(host_bits(case.decode()))
+    ref = _oracle_decode(w, kc, vc, seqs=seqs)
+    ma, mr = assert_close(got[seqs], ref[seqs], *TOL["bf16"], what="qwen3-8b sampled")
+    print(f"[qwen3-8b decode, {len(seqs)} sampled] max_abs={ma:.3e} max_rel={mr:.3e}")
+    # the sampled sequences' blocks hold exactly the oracle's bytes at valid positions
+    for s in seqs[:4]:
+        n = int(lens[s])
+        Kg, Vg = oracle.cache.depage_raw(host_bits(case.k_cache[torch.as_tensor(blocks).cuda()]),
+                                         host_bits(case.v_cache[torch.as_tensor(blocks).cuda()]),
+                                         np.searchsorted(blocks, w.block_tables[s]), n, w.block_size)
+        Ko, Vo = oracle.cache.depage_raw(kc, vc, w.block_tables[s], n, w.block_size)
+        assert np.array_equal(Kg, Ko) and np.array_equal(Vg, Vo)
+
+
+def test_fp8_long_context_sampled():
+    w = W.make(5)
+    case = GpuCase(w)
+    lens = w.context_lens
+    seqs = sorted({int(lens.argmax()), int(lens.argmin()), 0, 1, 17, 40})
+    kc, vc, blocks = _oracle_pools_for(w, seqs)
+    got = bf16_f64(host_bits(case.decode()))
+    ref = _oracle_decode(w, kc, vc, seqs=seqs)
+    ma, mr = assert_close(got[seqs], ref[seqs], *TOL["fp8"], what="fp8 long sampled")
+    print(f"[fp8 long decode, {len(seqs)} sampled] max_abs={ma:.3e} max_rel={mr:.3e}")
+    for s in seqs[:3]:
+        n = int(lens[s])
+        idx = torch.as_tensor(blocks).cuda()
+        Kg, Vg = oracle.cache.depage_raw(host_bits(case.k_cache[idx]), host_bits(case.v_cache[idx]),
+                                         np.searchsorted(blocks, w.block_tables[s]), n, w.block_size)
+        Ko, Vo = oracle.cache.depage_raw(kc, vc, w.block_tables[s], n, w.block_size)
+        assert np.array_equal(Kg, Ko) and np.array_equal(Vg, Vo)
+
+
+# ---------------------------------------------------------------- invariants and closed forms
+def test_context_one_returns_v_exactly():
+    w = W.custom(seed=201, Hq=8, Hkv=2, D=128, bs=16, context_lens=(1, 1, 1))
+    case = GpuCase(w)
+    out = host_bits(case.decode())
+    expect = np.repeat(w.new_v, 4, axis=1)          # query head h reads KV head h // 4
+    assert np.array_equal(out, expect)
+
+
+def test_block_permutation_bit_identical():
+    w = W.custom(seed=202, Hq=8, Hkv=2, D=128, bs=32, context_lens=(7, 90, 300, 1500),
+                 partition_size=256)
+    a = host_bits(GpuCase(w).decode())
+    b = host_bits(GpuCase(relabel_blocks(w, seed=4)).decode())
+    assert np.array_equal(a, b)
+
+
+def test_shared_prefix_equals_private_copies_bit_identical():
+    w = W.custom(seed=203, Hq=8, Hkv=2, D=128, bs=64, context_lens=(300, 400, 500),
+                 sharers=(0, 1, 2), shared_prefix_blocks=2, num_blocks=40)
+    case = GpuCase(w)
+    shared = host_bits(case.decode())
+    bt = w.block_tables.copy()
+    free = list(w.unused_blocks[1:])
+    for s in (1, 2):
+        for j in range(2):
+            nb = int(free.pop())
+            case.k_cache[nb] = case.k_cache[int(bt[s, j])]
+            case.v_cache[nb] = case.v_cache[int(bt[s, j])]
+            bt[s, j] = nb
+    case.block_tables = torch.from_numpy(bt).cuda()
+    private = host_bits(case.decode())
+    assert np.array_equal(shared, private)
+
+
+def test_split_matches_single_partition():
+    w = W.custom(seed=204, Hq=32, Hkv=8, D=128, bs=256, context_lens=(3000, 4096, 999, 2500))
+    case = GpuCase(w)
+    one = bf16_f64(host_bits(case.decode(partition_size=4096)))
+    for ps in (256, 512, 1024):
+        split = bf16_f64(host_bits(case.decode(partition_size=ps)))
+        # same arithmetic up to float32 rounding order, then one bf16 rounding each
+        np.testing.assert_allclose(split, one, rtol=2 ** -7, atol=1e-3)
+
+
+def test_deterministic_and_guard_bands():
+    w = W.custom(seed=205, Hq=16, Hkv=8, D=128, bs=256, context_lens=(100, 1024, 3000),
+                 partition_size=512)
+    case = GpuCase(w)
+    S, Hq, D = w.q.shape
+    buf = torch.full((S + 2, Hq, D), 1234.0, dtype=torch.bfloat16, device="cuda")
+    case.decode(out=buf[1:S + 1])
+    first = host_bits(buf)
+    case.decode(out=buf[1:S + 1])
+    second = host_bits(buf)
+    assert np.array_equal(first, second)
+    sentinel = host_bits(torch.full((Hq, D), 1234.0, dtype=torch.bfloat16))
+    assert np.array_equal(first[0], sentinel) and np.array_equal(first[S + 1], sentinel)
+
+
+def test_store_skips_negative_and_out_of_range_slots():
+    w = W.custom(seed=206, Hq=4, Hkv=2, D=64, bs=16, context_lens=(40, 9))
+    case = GpuCase(w, store_new=False)
+    before_k, before_v = host_bits(case.k_cache), host_bits(case.v_cache)
+    slots = w.new_slots.copy()
+    slots[0::2] = -1
+    slots[1::2] = w.num_blocks * w.block_size + 5
+    case.store(case.new_k, case.new_v, torch.from_numpy(slots).cuda())
+    assert np.array_equal(host_bits(case.k_cache), before_k)
+    assert np.array_equal(host_bits(case.v_cache), before_v)
+
+
+def test_wrapper_rejects_bad_arguments():
+    import paged_kv_cache_store_amd as pa
+    w = W.custom(seed=207, Hq=4, Hkv=2, D=64, bs=16, context_lens=(5,))
+    case = GpuCase(w)
+    with pytest.raises(ValueError):
+        pa.decode(case.q.float(), case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                  0.125, 5)
+    with pytest.raises(pa.PaError):
+        pa.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, 0.125, 5,
+                  partition_size=100)
