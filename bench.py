@@ -224,6 +224,26 @@ def _oracle_baseline(w, budget_s=12.0):
             "seconds": round(t_total, 2)}
 
 
+def copy_calibration(torch, reps):
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "read_plus_write_TBps": round(2 * n / (ms * 1e-3) / 1e12, 4)}), flush=True)
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -235,6 +255,8 @@ def main():
                     help="decode partition size (default: the workload's, else automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="time a plain 1 GiB device copy (counter calibration / HBM ceiling) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("this build runs on one GPU only: --gpus must be 1 (no multi-GPU path exists)",
@@ -246,6 +268,9 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calib:
+        copy_calibration(torch, args.steps)
+        return
 
     def measure(number, steps, warmup):
         w = W.make(number)

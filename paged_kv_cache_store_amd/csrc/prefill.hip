@@ -1,12 +1,357 @@
-// Causal varlen prefill over the paged cache (placeholder until the MFMA kernel).
+// Causal varlen prefill over the paged KV cache, on the matrix cores.
+//
+// Chunked prefill splits a long prompt into chunks that run next to decode; a
+// chunk's queries attend to the sequence's cached prefix plus the chunk itself,
+// and prefill is compute-bound ("nano-vllm-lite：深入理解LLM推理机制的教育级开源项目",
+// 核心技术改进 §2). The keys/values come from the block pool through the block
+// table ("DeepSeek复刻vLLM反超原版：AI推理新标杆", section vLLM：大模型推理的加速引擎与挑战);
+// the attention is exact, computed tile by tile with a running max and sum
+// ("Nano-vLLM：轻量高效的大模型推理框架…", 三.3 模型层适配).
+//
+// Work decomposition (CDNA4, wave64, v_mfma_f32_32x32x16_bf16):
+// * one workgroup (4 waves) per (sequence, KV head, block of 256/G query rows);
+//   the G query heads of the KV head are packed into 256 rows, 64 per wave, so
+//   every K/V tile staged in LDS serves all G heads;
+// * K/V tiles of 64 keys are copied from the pool to LDS in the pool's own
+//   16-byte layout (double-buffered through registers): K as [D/8][64][8],
+//   V as [8][D][8] (8 consecutive keys of one head-dim index per 16 bytes);
+// * S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T from registers (loaded
+//   once), so each lane owns one query column and its softmax statistics;
+// * the row max needs one exchange with lane l^32; the weights P^T come out of
+//   the accumulator already in the B-operand layout of the next product;
+// * O^T += V^T P^T: A = V^T from LDS (two 8-byte reads per fragment because the
+//   accumulator's key order is {4h..4h+3, 8+4h..8+4h+3} per lane half h).
+#include <math.h>
+
+#include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
-hipError_t launch_prefill(const uint16_t*, const uint8_t*, const uint8_t*, const int32_t*,
-                          const int32_t*, const int32_t*, int, int, int, int, int, float,
-                          uint16_t*, const PoolDims&, hipStream_t) {
-  return hipErrorNotSupported;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kPrefillThreads = 256;
+constexpr int kPackedRows = 256;  // query rows x heads per workgroup
+constexpr int kBN = 64;           // keys per tile
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* block_tables;
+  uint16_t* out;
+  int max_blocks_per_seq;
+  int num_seqs;
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int max_seqlen_q;
+  int cap_k;
+  int num_qblocks;
+  float scale_log2;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ float xor32(float x) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), 32));
+}
+
+template <int kD, int kG>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillArgs a) {
+  constexpr int kBM = kPackedRows / kG;  // query rows per workgroup
+  constexpr int kKS = kD / 16;           // k-steps of S^T = K Q^T
+  constexpr int kDB = kD / 32;           // 32-row blocks of O^T
+  constexpr int kKC = kD / 8;            // 16-byte chunks per key
+  constexpr int kKLoads = kKC * kBN / kPrefillThreads;   // 16-byte K loads per thread per tile
+  constexpr int kVLoads = (kBN / 8) * kD / kPrefillThreads;
+
+  __shared__ uint4 k_s[2][kKC][kBN];
+  __shared__ uint4 v_s[2][kBN / 8][kD];
+
+  const int Hkv = a.num_kv_heads;
+  const int bid = blockIdx.x;
+  const int hk = bid % Hkv;
+  const int rest = bid / Hkv;
+  // later query blocks and later sequences usually see more keys: start them first
+  const int qb = a.num_qblocks - 1 - rest % a.num_qblocks;
+  const int s = a.num_seqs - 1 - rest / a.num_qblocks;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane % 32;
+  const int half = lane / 32;
+
+  const int q0 = a.cu_q[s];
+  int Lq = a.cu_q[s + 1] - q0;
+  Lq = Lq < a.max_seqlen_q ? Lq : a.max_seqlen_q;
+  int Lk = a.cu_k[s + 1] - a.cu_k[s];
+  Lk = Lk < a.cap_k ? Lk : a.cap_k;
+  const int row0 = qb * kBM;
+  if (row0 >= Lq || Lq <= 0) return;
+  const int bs = a.block_size;
+  const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq;
+  const long long slab16 = (long long)bs * kD * 2 / 16;
+  const uint4* kpool = reinterpret_cast<const uint4*>(a.k_cache) + (long long)hk * slab16;
+  const uint4* vpool = reinterpret_cast<const uint4*>(a.v_cache) + (long long)hk * slab16;
+  const long long blk16 = (long long)Hkv * slab16;
+
+  // ---- this wave's two 32-column blocks: (query head, first query row)
+  int head[2], qrow[2], lim[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int pr = w * 64 + nb * 32;
+    head[nb] = hk * kG + pr / kBM;
+    qrow[nb] = row0 + pr % kBM + l32;                      // this lane's query row
+    const int last = Lk - Lq + qrow[nb];                   // last key it may see
+    lim[nb] = last < Lk - 1 ? last : Lk - 1;
+  }
+  // keys this wave needs: up to the largest limit of its rows
+  int wave_last = -1;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = row0 + (w * 64 + nb * 32) % kBM + 31;
+    const int last = Lk - Lq + (r < Lq - 1 ? r : Lq - 1);
+    const int lc = last < Lk - 1 ? last : Lk - 1;
+    wave_last = lc > wave_last ? lc : wave_last;
+  }
+  // keys the workgroup needs
+  int wg_last = Lk - Lq + (row0 + kBM - 1 < Lq - 1 ? row0 + kBM - 1 : Lq - 1);
+  wg_last = wg_last < Lk - 1 ? wg_last : Lk - 1;
+  const int ntiles = wg_last >= 0 ? (wg_last + kBN) / kBN : 0;
+
+  // ---- Q^T fragments (B operand): lane holds column qrow, head-dim 16*ks + 8*half .. +8
+  uint4 qf[2][kKS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = qrow[nb] < Lq ? qrow[nb] : Lq - 1;
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((long long)(q0 + r) * a.num_q_heads + head[nb]) * kD);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[nb][ks] = qp[ks * 2 + half];
+  }
+
+  // ---- tile loader: pool -> registers -> LDS
+  uint4 kreg[kKLoads], vreg[kVLoads];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int u = 0; u < kKLoads; ++u) {
+      const int idx = u * kPrefillThreads + tid;
+      const int c = idx / kBN;
+      const int key = kt * kBN + idx % kBN;
+      const int kc = key < Lk ? key : Lk - 1;
+      const uint4* src = kpool + bt[kc / bs] * blk16 + (long long)c * bs + kc % bs;
+      uint4 v = *src;
+      if (key >= Lk) v = make_uint4(0u, 0u, 0u, 0u);
+      kreg[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) {
+      const int idx = u * kPrefillThreads + tid;
+      const int j = idx / kD;       // 8-key chunk of the tile
+      const int d = idx % kD;
+      const int key = kt * kBN + j * 8;
+      const int kc = key < Lk ? key : ((Lk - 1) & ~7);
+      const uint4* src = vpool + bt[kc / bs] * blk16 + (long long)((kc % bs) / 8) * kD + d;
+      uint4 v = *src;
+      const int nv = Lk - key;      // valid keys in this chunk
+      if (nv < 8) {
+        uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          e[i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+        v = make_uint4(e[0], e[1], e[2], e[3]);
+      }
+      vreg[u] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kKLoads; ++u) {
+      const int idx = u * kPrefillThreads + tid;
+      k_s[buf][idx / kBN][idx % kBN] = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) {
+      const int idx = u * kPrefillThreads + tid;
+      v_s[buf][idx / kD][idx % kD] = vreg[u];
+    }
+  };
+
+  f32x16_t o[kDB][2];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][nb][i] = 0.f;
+  float m[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  const float sc = a.scale_log2;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+    const int key0 = kt * kBN;
+    if (key0 <= wave_last) {
+      // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
+      f32x16_t sacc[2][2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8_t af = as_bf16x8(k_s[buf][ks * 2 + half][mb * 32 + l32]);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(qf[nb][ks]),
+                                                                   sacc[mb][nb], 0, 0, 0);
+        }
+      }
+      // ---- online softmax per query column; build P^T in the B-operand layout
+      uint4 pf[2][4];   // [nb][16-key step]
+      const bool diag = key0 + kBN - 1 > lim[0] || key0 + kBN - 1 > lim[1];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float x[2][16];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+            float v = sacc[mb][nb][i] * sc;
+            if (diag && key > lim[nb]) v = -INFINITY;
+            x[mb][i] = v;
+            mt = fmaxf(mt, v);
+          }
+        mt = fmaxf(mt, xor32(mt));
+        const float mn = fmaxf(m[nb], mt);
+        // a column that has seen no key yet keeps max -inf; its weights stay 0
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m[nb] - mref);
+        m[nb] = mn;
+        float ps = 0.f;
+        uint32_t packed[2][8];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const uint32_t lo = f32_to_bf16(fast_exp2(x[mb][i] - mref));
+            const uint32_t hi = f32_to_bf16(fast_exp2(x[mb][i + 1] - mref));
+            ps += bf16_lo(lo) + bf16_lo(hi);
+            packed[mb][i / 2] = lo | (hi << 16);
+          }
+        lsum[nb] = lsum[nb] * alpha + ps;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
+        // B operand of the 16-key step t = 2*mb + j: accumulator entries 8j .. 8j+7
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            pf[nb][2 * mb + j] = make_uint4(packed[mb][4 * j], packed[mb][4 * j + 1],
+                                            packed[mb][4 * j + 2], packed[mb][4 * j + 3]);
+      }
+      // ---- O^T += V^T P^T; step t covers tile keys 16t + {4h..4h+3, 8+4h..8+4h+3}
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d = db * 32 + l32;
+          const uint2* c0 = reinterpret_cast<const uint2*>(&v_s[buf][2 * t][d]);
+          const uint2* c1 = reinterpret_cast<const uint2*>(&v_s[buf][2 * t + 1][d]);
+          const uint2 lo = c0[half];
+          const uint2 hi = c1[half];
+          const bf16x8_t af = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
+                                                                0, 0, 0);
+        }
+      }
+    }
+    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and write this lane's query rows
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const float L = lsum[nb] + xor32(lsum[nb]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (qrow[nb] < Lq) {
+      uint16_t* op = a.out + ((long long)(q0 + qrow[nb]) * a.num_q_heads + head[nb]) * kD;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + half * 4;
+          const uint32_t b0 = f32_to_bf16(o[db][nb][4 * g4 + 0] * inv);
+          const uint32_t b1 = f32_to_bf16(o[db][nb][4 * g4 + 1] * inv);
+          const uint32_t b2 = f32_to_bf16(o[db][nb][4 * g4 + 2] * inv);
+          const uint32_t b3 = f32_to_bf16(o[db][nb][4 * g4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        }
+    }
+  }
+}
+
+template <int kD>
+static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
+  switch (G) {
+    case 1: prefill_kernel<kD, 1><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 2: prefill_kernel<kD, 2><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 4: prefill_kernel<kD, 4><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 8: prefill_kernel<kD, 8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    default: return false;
+  }
+}
+
+hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_tables,
+                          int max_blocks_per_seq, int num_seqs, int num_q_heads,
+                          int max_seqlen_q, int max_seqlen_k, float scale, uint16_t* out,
+                          const PoolDims& pool, hipStream_t stream) {
+  const int G = num_q_heads / pool.num_kv_heads;
+  const int bm = kPackedRows / G;
+  PrefillArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.block_tables = block_tables;
+  a.out = out;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool.num_kv_heads;
+  a.block_size = pool.block_size;
+  a.max_seqlen_q = max_seqlen_q;
+  a.cap_k = max_seqlen_k;
+  a.num_qblocks = (max_seqlen_q + bm - 1) / bm;
+  a.scale_log2 = scale * kLog2e;
+  const unsigned grid = unsigned((long long)num_seqs * a.num_qblocks * pool.num_kv_heads);
+  if (grid == 0) return hipSuccess;
+  const bool ok = pool.head_dim == 64 ? launch_prefill_g<64>(G, a, grid, stream)
+                                      : launch_prefill_g<128>(G, a, grid, stream);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -1,0 +1,103 @@
+"""GPU parity of pa_prefill_varlen (causal varlen chunked prefill over the paged
+cache, MFMA) against the CPU oracle, plus invariants. Tolerance: element-wise
+|gpu - oracle| <= 1e-2 + 1e-2*|oracle| (bf16 cache, float32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import GpuCase, dev_bf16, dev_i32, host_bits
+from tests.util import assert_close, bf16_f64, oracle_pools, relabel_blocks
+
+pytestmark = pytest.mark.gpu
+
+TOL = (1e-2, 1e-2)
+
+
+def _oracle_prefill(w, kc, vc, seqs=None):
+    return oracle.attention.prefill(w.pq, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.p_block_tables,
+                                    w.scale, w.block_size, seqs=seqs)
+
+
+CASES = [
+    dict(seed=301, Hq=4, Hkv=1, D=128, bs=16, prefill=[(0, 1), (0, 17), (0, 64), (0, 65), (16, 16)]),
+    dict(seed=302, Hq=8, Hkv=2, D=128, bs=64, prefill=[(100, 30), (37, 200), (0, 300), (256, 64)]),
+    dict(seed=303, Hq=32, Hkv=8, D=128, bs=256, prefill=[(0, 512), (768, 512), (1000, 77)]),
+    dict(seed=304, Hq=16, Hkv=8, D=64, bs=32, prefill=[(5, 250), (0, 129), (300, 1)]),
+    dict(seed=305, Hq=8, Hkv=1, D=64, bs=128, prefill=[(0, 40), (200, 33), (64, 70)]),
+    dict(seed=306, Hq=2, Hkv=2, D=128, bs=16, prefill=[(0, 300), (513, 260)]),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_prefill_small(cfg):
+    print(f"case {cfg}", flush=True)
+    w = W.custom(context_lens=(), **cfg)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    got = bf16_f64(host_bits(case.prefill()))
+    ma, mr = assert_close(got, _oracle_prefill(w, kc, vc), *TOL, what="prefill")
+    print(f"max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_mixed_chunked_prefill_workload():
+    """Full mixed step: store of 4344 tokens, prefill of the 8 chunks (all rows checked),
+    decode of the 248 sequences (all checked)."""
+    w = W.make(4)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    pre = bf16_f64(host_bits(case.prefill()))
+    ma, mr = assert_close(pre, _oracle_prefill(w, kc, vc), *TOL, what="mixed prefill")
+    print(f"[mixed prefill] max_abs={ma:.3e} max_rel={mr:.3e}")
+    dec = bf16_f64(host_bits(case.decode()))
+    ref = oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.block_size)
+    ma, mr = assert_close(dec, ref, *TOL, what="mixed decode")
+    print(f"[mixed decode] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_chunk_equals_tail_of_full_prefill_bit_identical():
+    """Prefill of a 96-token chunk on a 160-token cached prefix gives the last 96 rows of
+    the prefill of all 256 tokens (same per-row arithmetic)."""
+    p, c = 160, 96
+    w = W.custom(seed=310, Hq=8, Hkv=2, D=128, bs=64, context_lens=(), prefill=[(p, c)])
+    case = GpuCase(w)
+    chunk = host_bits(case.prefill())
+    rng = np.random.default_rng(1)
+    qfull = np.concatenate([W.f32_to_bf16_bits(rng.standard_normal((p, 8, 128)).astype(np.float32)), w.pq])
+    import paged_kv_cache_store_amd as pa
+    full = pa.prefill_varlen(dev_bf16(qfull), case.k_cache, case.v_cache, dev_i32([0, p + c]),
+                             dev_i32([0, p + c]), case.p_block_tables, float(w.scale), p + c, p + c)
+    assert np.array_equal(host_bits(full)[p:], chunk)
+
+
+def test_prefill_block_permutation_bit_identical():
+    w = W.custom(seed=311, Hq=8, Hkv=2, D=128, bs=32, context_lens=(), prefill=[(70, 100), (0, 33)])
+    a = host_bits(GpuCase(w).prefill())
+    b = host_bits(GpuCase(relabel_blocks(w, seed=2)).prefill())
+    assert np.array_equal(a, b)
+
+
+def test_decode_matches_one_row_prefill():
+    w = W.custom(seed=312, Hq=16, Hkv=4, D=128, bs=64, context_lens=(1, 100, 700))
+    case = GpuCase(w)
+    dec = bf16_f64(host_bits(case.decode()))
+    import paged_kv_cache_store_amd as pa
+    S = w.num_seqs
+    cu_k = np.concatenate([[0], np.cumsum(w.context_lens)])
+    pre = pa.prefill_varlen(case.q, case.k_cache, case.v_cache, dev_i32(np.arange(S + 1)), dev_i32(cu_k),
+                            case.block_tables, float(w.scale), 1, int(w.context_lens.max()))
+    np.testing.assert_allclose(bf16_f64(host_bits(pre)), dec, rtol=2 ** -7, atol=2e-3)
+
+
+def test_prefill_guard_bands_and_determinism():
+    w = W.custom(seed=313, Hq=8, Hkv=2, D=64, bs=16, context_lens=(), prefill=[(20, 45)])
+    case = GpuCase(w)
+    Tq, Hq, D = w.pq.shape
+    buf = torch.full((Tq + 2, Hq, D), -7.0, dtype=torch.bfloat16, device="cuda")
+    case.prefill(out=buf[1:Tq + 1])
+    first = host_bits(buf)
+    case.prefill(out=buf[1:Tq + 1])
+    assert np.array_equal(first, host_bits(buf))
+    sentinel = host_bits(torch.full((Hq, D), -7.0, dtype=torch.bfloat16))
+    assert np.array_equal(first[0], sentinel) and np.array_equal(first[Tq + 1], sentinel)
