@@ -101,7 +101,9 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
 
-/* Partition size pa_decode uses for these bounds (resolves 0 = automatic). */
+/* Partition size pa_decode uses for these bounds (resolves 0 = automatic: whole
+ * contexts when num_seqs*num_q_heads >= 4096, else partitions of up to 2048
+ * tokens; never above 4096). */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t max_context_len, int32_t partition_size);
 
@@ -146,6 +148,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   max_seqlen_q, max_seqlen_k  host bounds >= every Lq, Lk; Lq is clamped to
  *                 max_seqlen_q and Lk to min(max_seqlen_k, max_blocks_per_seq*block_size)
+ *   scale         softmax scale, finite and > 0 (else PA_ERR_SHAPE)
  *   out           device bf16 [total_q][num_q_heads][head_dim]
  * Query i of sequence s sits at position Lk-Lq+i and attends to keys 0..Lk-Lq+i
  * (mask aligned bottom-right); a row that sees no key is written as zeros. */

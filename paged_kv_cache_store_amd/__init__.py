@@ -19,7 +19,8 @@ import torch
 __all__ = ["store_kv", "decode", "prefill_varlen", "decode_workspace_size",
            "decode_partition_size", "empty_pools", "PaError", "LIB_PATH", "library"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIBRARY may point at another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
 
@@ -219,7 +220,8 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
 
 def header_functions(header_path=None):
     """Names of the functions include/pa.h declares."""
-    path = header_path or os.path.join(os.path.dirname(os.path.dirname(LIB_PATH)), "include", "pa.h")
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = header_path or os.path.join(os.path.dirname(here), "include", "pa.h")
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))

@@ -42,13 +42,14 @@ def _run(cmd):
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so; returns the library path."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source and link libpa.so (or `out`); returns the library path.
+    `defines` are extra -D macros (tuning variants of the kernels)."""
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [HIPCC, *DEVICE_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+            cmd = [HIPCC, *DEVICE_FLAGS, *["-D" + d for d in defines], "-I", INCLUDE, "-I", CSRC, "-c",
                    os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd))
@@ -56,8 +57,8 @@ def build(verbose: bool = False) -> str:
             objs.append(obj)
         out_tmp = os.path.join(tmp, "libpa.so")
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp])
-        shutil.move(out_tmp, LIB)
-    return LIB
+        shutil.move(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,6 +1,7 @@
 // C ABI of libpa (declared in include/pa.h): argument checks, then launches.
 // Every check below runs on the host before anything is enqueued, so a bad
 // argument never reaches the GPU and the checks can be exercised without one.
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -41,13 +42,16 @@ bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
 
-// Automatic partition size: about four partitions for the longest context,
-// between 256 and 1024 tokens.
-int32_t auto_partition(int32_t max_context_len) {
-  int32_t p = round_up((max_context_len + 3) / 4, 256);
-  if (p < 256) p = 256;
-  if (p > 1024) p = 1024;
-  return p;
+// Automatic partition size. With enough (sequence, query head) rows to fill the
+// GPU, contexts stay whole (no partial results, no reduce); otherwise long
+// contexts are cut into 2048-token partitions. Never above 4096 tokens, so the
+// partition's block ids fit the 256-entry table in LDS for every block size.
+int32_t auto_partition(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len) {
+  int32_t whole = round_up(max_context_len, 256);
+  if (whole < 256) whole = 256;
+  const long long rows = (long long)num_seqs * num_q_heads;
+  const int32_t cap = rows >= 4096 ? 4096 : 2048;
+  return whole < cap ? whole : cap;
 }
 
 }  // namespace
@@ -86,10 +90,8 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
                                  int32_t partition_size) {
-  (void)num_seqs;
-  (void)num_q_heads;
   if (partition_size > 0) return partition_size;
-  return auto_partition(max_context_len < 0 ? 0 : max_context_len);
+  return auto_partition(num_seqs, num_q_heads, max_context_len < 0 ? 0 : max_context_len);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -148,7 +150,7 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
     return PA_ERR_SHAPE;
   if (num_q_heads % dims.num_kv_heads != 0) return PA_ERR_SHAPE;
   if (!supported_group(num_q_heads / dims.num_kv_heads)) return PA_ERR_UNSUPPORTED;
-  if (!(scale == scale)) return PA_ERR_SHAPE;
+  if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
     return PA_ERR_NULL;

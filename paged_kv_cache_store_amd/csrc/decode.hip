@@ -33,7 +33,14 @@
 
 namespace pa {
 
-constexpr int kDecodeThreads = 256;
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_WAVES_PER_EU
+#define PA_DECODE_WAVES_PER_EU 0
+#endif
+
+constexpr int kDecodeThreads = PA_DECODE_WAVES * 64;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kTile = 64;            // keys per wave per step
 constexpr int kMaxPartBlocks = 256;  // block ids per partition staged in LDS
@@ -61,7 +68,11 @@ struct DecodeArgs {
 };
 
 template <int kD, int kG, bool kFp8>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads)
+#if PA_DECODE_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
+#endif
+void decode_kernel(const DecodeArgs a) {
   constexpr int kX = kFp8 ? 16 : 8;       // elements per 16-byte chunk
   constexpr int kKC = kD / kX;            // K chunks per key
   constexpr int kVC = kTile / kX;         // V key-chunks per tile
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   const int nb = (pend - p0 + bs - 1) / bs;
   const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq + p0 / bs;
   for (int i = tid; i < nb; i += kDecodeThreads) blk_s[i] = bt[i];
-  __syncthreads();
+  if (kDecodeWaves > 1) __syncthreads();
 
   const uint32_t* qg =
       reinterpret_cast<const uint32_t*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD);
@@ -125,28 +136,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
   }
 
   const int ntiles = (pend - p0 + kTile - 1) / kTile;
-  for (int t = w; t < ntiles; t += kDecodeWaves) {
+
+  // ---- loads of one tile: K with lane = key, V with lane = head-dim index.
+  // Streaming, read-once data: non-temporal loads.
+  auto load_tile = [&](int t, uint4 (&kr)[kKC], uint4 (&vr)[kVC][kDL]) {
     const int key0 = p0 + t * kTile;
     const int key = key0 + lane;
-    const bool valid = key < pend;
-    // ---- issue all loads of the tile: K (lane = key), V (lane = head-dim index)
-    uint4 kr[kKC];
-    {
-      const int rel = (valid ? key : pend - 1) - p0;
-      const uint4* kp = kbase + blk_s[rel / bs] * blk_stride16 + (rel % bs);
+    const int rel = (key < pend ? key : pend - 1) - p0;
+    const uint4* kp = kbase + blk_s[rel / bs] * blk_stride16 + (rel % bs);
 #pragma unroll
-      for (int c = 0; c < kKC; ++c) kr[c] = kp[(long long)c * bs];
-    }
-    uint4 vr[kVC][kDL];
+    for (int c = 0; c < kKC; ++c) kr[c] = load_nt(kp + (long long)c * bs);
 #pragma unroll
     for (int j = 0; j < kVC; ++j) {
       int kk = key0 + j * kX;
       if (kk >= pend) kk = (pend - 1) & ~(kX - 1);  // stay inside written blocks; result unused
-      const int rel = kk - p0;
-      const uint4* vp = vbase + blk_s[rel / bs] * blk_stride16 + (long long)((rel % bs) / kX) * kD;
+      const int vrel = kk - p0;
+      const uint4* vp = vbase + blk_s[vrel / bs] * blk_stride16 + (long long)((vrel % bs) / kX) * kD;
 #pragma unroll
-      for (int dl = 0; dl < kDL; ++dl) vr[j][dl] = vp[lane + dl * kWave];
+      for (int dl = 0; dl < kDL; ++dl) vr[j][dl] = load_nt(vp + lane + dl * kWave);
     }
+  };
+
+  auto compute_tile = [&](int t, const uint4 (&kr)[kKC], const uint4 (&vr)[kVC][kDL]) {
+    const int key0 = p0 + t * kTile;
+    const bool valid = key0 + lane < pend;
     // ---- scores
     float sv[kG];
 #pragma unroll
@@ -242,9 +255,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const DecodeArgs
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  for (int t = w; t < ntiles; t += kDecodeWaves) {
+    uint4 kr[kKC], vr[kVC][kDL];
+    load_tile(t, kr, vr);
+    compute_tile(t, kr, vr);
   }
 
-  // ---- merge the 4 waves
+  // ---- merge the waves
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     const float lw = wave_sum(l[g]);

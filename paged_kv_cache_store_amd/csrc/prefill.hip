@@ -56,9 +56,22 @@ struct PrefillArgs {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__device__ __forceinline__ float xor32(float x) {
-  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), 32));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// max / sum of x over lanes l and l^32 (v_permlane32_swap: the returned pair
+// holds x of lanes l%32 and l%32+32, for every lane)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int kD, int kG>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillArgs a) {
@@ -117,6 +130,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
     const int last = Lk - Lq + (r < Lq - 1 ? r : Lq - 1);
     const int lc = last < Lk - 1 ? last : Lk - 1;
     wave_last = lc > wave_last ? lc : wave_last;
+  }
+  // smallest limit among this wave's columns (limits grow with the row)
+  int wave_lim_min = 1 << 30;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = row0 + (w * 64 + nb * 32) % kBM;
+    int lm = Lk - Lq + r;
+    lm = lm < Lk - 1 ? lm : Lk - 1;
+    wave_lim_min = lm < wave_lim_min ? lm : wave_lim_min;
   }
   // keys the workgroup needs
   int wg_last = Lk - Lq + (row0 + kBM - 1 < Lq - 1 ? row0 + kBM - 1 : Lq - 1);
@@ -220,45 +242,58 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
                                                                    sacc[mb][nb], 0, 0, 0);
         }
       }
-      // ---- online softmax per query column; build P^T in the B-operand layout
+      // ---- online softmax per query column; build P^T in the B-operand layout.
+      // Scores stay unscaled until one fma + exp2 per element. The reference max
+      // m of a column only moves when the tile's max exceeds it by more than 8
+      // (log2 units), so weights stay <= 2^8 and O, l are rescaled rarely; O and
+      // l share the reference, so the normalised result is unchanged.
       uint4 pf[2][4];   // [nb][16-key step]
-      const bool diag = key0 + kBN - 1 > lim[0] || key0 + kBN - 1 > lim[1];
+      const bool diag_tile = key0 + kBN - 1 > wave_lim_min;  // some column masks keys here
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        float x[2][16];
-        float mt = -INFINITY;
+        if (diag_tile) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+              if (key > lim[nb]) sacc[mb][nb][i] = -INFINITY;
+            }
+        }
+        float smax = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-            float v = sacc[mb][nb][i] * sc;
-            if (diag && key > lim[nb]) v = -INFINITY;
-            x[mb][i] = v;
-            mt = fmaxf(mt, v);
-          }
-        mt = fmaxf(mt, xor32(mt));
-        const float mn = fmaxf(m[nb], mt);
-        // a column that has seen no key yet keeps max -inf; its weights stay 0
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m[nb] - mref);
-        m[nb] = mn;
-        float ps = 0.f;
+          for (int i = 0; i < 16; i += 2) smax = fmaxf(smax, fmaxf(sacc[mb][nb][i], sacc[mb][nb][i + 1]));
+        smax = pair_max(smax);
+        const float mt = smax * sc;                  // sc > 0: -inf stays -inf
+        const bool grow = mt > m[nb] + 8.f;
+        if (__any(grow)) {
+          const float mn = grow ? mt : m[nb];
+          const float alpha = fast_exp2(m[nb] - mn);  // 0 the first time (O, l are 0)
+          lsum[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
+          m[nb] = mn;
+        }
+        // a column with no admissible key yet keeps m = -inf; its weights are 0
+        const float mneg = m[nb] == -INFINITY ? 0.f : -m[nb];
         uint32_t packed[2][8];
+        float ps = lsum[nb];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
-            const uint32_t lo = f32_to_bf16(fast_exp2(x[mb][i] - mref));
-            const uint32_t hi = f32_to_bf16(fast_exp2(x[mb][i + 1] - mref));
-            ps += bf16_lo(lo) + bf16_lo(hi);
-            packed[mb][i / 2] = lo | (hi << 16);
+            f32x2_t pp;
+            pp.x = fast_exp2(fmaf(sacc[mb][nb][i], sc, mneg));
+            pp.y = fast_exp2(fmaf(sacc[mb][nb][i + 1], sc, mneg));
+            const bf16x2_t pk = __builtin_convertvector(pp, bf16x2_t);
+            ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnesBf16x2, ps, false);  // sum of the bf16 weights
+            packed[mb][i / 2] = __builtin_bit_cast(uint32_t, pk);
           }
-        lsum[nb] = lsum[nb] * alpha + ps;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
+        lsum[nb] = ps;
         // B operand of the 16-key step t = 2*mb + j: accumulator entries 8j .. 8j+7
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -292,7 +327,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
   // ---- normalise and write this lane's query rows
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float L = lsum[nb] + xor32(lsum[nb]);
+    const float L = pair_sum(lsum[nb]);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (qrow[nb] < Lq) {
       uint16_t* op = a.out + ((long long)(q0 + qrow[nb]) * a.num_q_heads + head[nb]) * kD;

@@ -80,13 +80,16 @@ def test_workspace_and_partition_rules(lib):
     assert lib.pa_decode_partition_size(64, 32, 32768, 1024) == 1024
     for ctx in (1, 100, 1016, 2042, 32657):
         p = lib.pa_decode_partition_size(1, 1, ctx, 0)
-        assert p % 256 == 0 and 256 <= p <= 1024
+        assert p % 256 == 0 and 256 <= p <= 2048
+        assert lib.pa_decode_partition_size(1024, 32, ctx, 0) == min(4096, max(256, -(-ctx // 256) * 256))
+    assert lib.pa_decode_partition_size(256, 16, 1016, 0) == 1024      # contexts kept whole
+    assert lib.pa_decode_partition_size(64, 32, 32657, 0) == 2048      # few rows: split
     P = lib.pa_decode_partition_size(64, 32, 32768, 0)
     assert lib.pa_decode_workspace_size(64, 32, 128, 32768, 0) == 64 * 32 * (32768 // P) * 130 * 4
 
 
-def prefill(lib, d, q=FAKE, S=2, hq=4, mq=16, mk=64, mb=8):
-    return lib.pa_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, FAKE, mb, S, hq, mq, mk, 0.125, FAKE,
+def prefill(lib, d, q=FAKE, S=2, hq=4, mq=16, mk=64, mb=8, scale=0.125):
+    return lib.pa_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, FAKE, mb, S, hq, mq, mk, scale, FAKE,
                                  ctypes.byref(d) if d is not None else None, None)
 
 
@@ -97,3 +100,5 @@ def test_prefill_validation(lib):
     assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE)) == UNSUP      # fp8 prefill not built
     assert prefill(lib, desc(), mq=-1) == SHAPE
     assert prefill(lib, desc(), S=0, q=None) == OK
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        assert prefill(lib, desc(), scale=bad) == SHAPE
