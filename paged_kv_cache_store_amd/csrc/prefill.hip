@@ -31,8 +31,15 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+#ifndef PA_PREFILL_NB
+#define PA_PREFILL_NB 1
+#endif
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 2
+#endif
+
 constexpr int kPrefillThreads = 256;
-constexpr int kPackedRows = 256;  // query rows x heads per workgroup
+constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kBN = 64;           // keys per tile
 
 struct PrefillArgs {
@@ -73,9 +80,16 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-template <int kD, int kG>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillArgs a) {
-  constexpr int kBM = kPackedRows / kG;  // query rows per workgroup
+// kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
+// (query row, head) columns, i.e. 128 * kNB / G query rows of each of the G heads.
+template <int kD, int kG, int kNB>
+__global__ __launch_bounds__(kPrefillThreads)
+#if PA_PREFILL_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
+#endif
+void prefill_kernel(const PrefillArgs a) {
+  constexpr int kCols = kPrefillWaves * 32 * kNB;
+  constexpr int kBM = kCols / kG;        // query rows per workgroup
   constexpr int kKS = kD / 16;           // k-steps of S^T = K Q^T
   constexpr int kDB = kD / 32;           // 32-row blocks of O^T
   constexpr int kKC = kD / 8;            // 16-byte chunks per key
@@ -112,43 +126,31 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
   const uint4* vpool = reinterpret_cast<const uint4*>(a.v_cache) + (long long)hk * slab16;
   const long long blk16 = (long long)Hkv * slab16;
 
-  // ---- this wave's two 32-column blocks: (query head, first query row)
-  int head[2], qrow[2], lim[2];
+  // ---- this lane's query columns: packed index -> (query head, query row)
+  int head[kNB], qrow[kNB], lim[kNB];
+  float lim_hi = -1.f, lim_lo = 1e30f;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int pr = w * 64 + nb * 32;
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int pr = (w * kNB + nb) * 32 + l32;
     head[nb] = hk * kG + pr / kBM;
-    qrow[nb] = row0 + pr % kBM + l32;                      // this lane's query row
-    const int last = Lk - Lq + qrow[nb];                   // last key it may see
+    qrow[nb] = row0 + pr % kBM;
+    const int last = Lk - Lq + qrow[nb];                   // last key the row may see
     lim[nb] = last < Lk - 1 ? last : Lk - 1;
+    const int rr = qrow[nb] < Lq - 1 ? qrow[nb] : Lq - 1;  // rows past Lq are not written
+    const int needed = Lk - Lq + rr < Lk - 1 ? Lk - Lq + rr : Lk - 1;
+    lim_hi = fmaxf(lim_hi, float(needed));
+    lim_lo = fminf(lim_lo, float(lim[nb]));
   }
-  // keys this wave needs: up to the largest limit of its rows
-  int wave_last = -1;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = row0 + (w * 64 + nb * 32) % kBM + 31;
-    const int last = Lk - Lq + (r < Lq - 1 ? r : Lq - 1);
-    const int lc = last < Lk - 1 ? last : Lk - 1;
-    wave_last = lc > wave_last ? lc : wave_last;
-  }
-  // smallest limit among this wave's columns (limits grow with the row)
-  int wave_lim_min = 1 << 30;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = row0 + (w * 64 + nb * 32) % kBM;
-    int lm = Lk - Lq + r;
-    lm = lm < Lk - 1 ? lm : Lk - 1;
-    wave_lim_min = lm < wave_lim_min ? lm : wave_lim_min;
-  }
+  const int wave_last = int(wave_max(lim_hi));          // keys this wave needs
+  const int wave_lim_min = int(-wave_max(-lim_lo));     // tiles below it need no mask
   // keys the workgroup needs
   int wg_last = Lk - Lq + (row0 + kBM - 1 < Lq - 1 ? row0 + kBM - 1 : Lq - 1);
   wg_last = wg_last < Lk - 1 ? wg_last : Lk - 1;
   const int ntiles = wg_last >= 0 ? (wg_last + kBN) / kBN : 0;
-
   // ---- Q^T fragments (B operand): lane holds column qrow, head-dim 16*ks + 8*half .. +8
-  uint4 qf[2][kKS];
+  uint4 qf[kNB][kKS];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     const int r = qrow[nb] < Lq ? qrow[nb] : Lq - 1;
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((long long)(q0 + r) * a.num_q_heads + head[nb]) * kD);
 #pragma unroll
@@ -202,15 +204,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
     }
   };
 
-  f32x16_t o[kDB][2];
+  f32x16_t o[kDB][kNB];
+  float m[kNB], lsum[kNB];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
+  for (int nb = 0; nb < kNB; ++nb) {
+    m[nb] = -INFINITY;
+    lsum[nb] = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][nb][i] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
+  }
   const float sc = a.scale_log2;
 
   if (ntiles > 0) {
@@ -224,11 +228,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
     const int key0 = kt * kBN;
     if (key0 <= wave_last) {
       // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
-      f32x16_t sacc[2][2];
+      f32x16_t sacc[2][kNB];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = 0.f;
 #pragma unroll
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
         for (int mb = 0; mb < 2; ++mb) {
           const bf16x8_t af = as_bf16x8(k_s[buf][ks * 2 + half][mb * 32 + l32]);
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < kNB; ++nb)
             sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(qf[nb][ks]),
                                                                    sacc[mb][nb], 0, 0, 0);
         }
@@ -247,10 +251,10 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
       // m of a column only moves when the tile's max exceeds it by more than 8
       // (log2 units), so weights stay <= 2^8 and O, l are rescaled rarely; O and
       // l share the reference, so the normalised result is unchanged.
-      uint4 pf[2][4];   // [nb][16-key step]
+      uint4 pf[kNB][4];   // [nb][16-key step]
       const bool diag_tile = key0 + kBN - 1 > wave_lim_min;  // some column masks keys here
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < kNB; ++nb) {
         if (diag_tile) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
           const uint2 hi = c1[half];
           const bf16x8_t af = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
+          for (int nb = 0; nb < kNB; ++nb)
             o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
                                                                 0, 0, 0);
         }
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
 
   // ---- normalise and write this lane's query rows
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     const float L = pair_sum(lsum[nb]);
     const float inv = L > 0.f ? 1.f / L : 0.f;
     if (qrow[nb] < Lq) {
@@ -346,13 +350,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(const PrefillA
   }
 }
 
+constexpr int kNBLaunch = PA_PREFILL_NB;
+
 template <int kD>
 static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   switch (G) {
-    case 1: prefill_kernel<kD, 1><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 2: prefill_kernel<kD, 2><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 4: prefill_kernel<kD, 4><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 8: prefill_kernel<kD, 8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 1: prefill_kernel<kD, 1, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 2: prefill_kernel<kD, 2, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 4: prefill_kernel<kD, 4, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 8: prefill_kernel<kD, 8, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
     default: return false;
   }
 }
@@ -363,7 +369,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
                           int max_seqlen_q, int max_seqlen_k, float scale, uint16_t* out,
                           const PoolDims& pool, hipStream_t stream) {
   const int G = num_q_heads / pool.num_kv_heads;
-  const int bm = kPackedRows / G;
+  const int bm = kPrefillWaves * 32 * kNBLaunch / G;
   PrefillArgs a;
   a.q = q;
   a.k_cache = k_cache;
