@@ -12,15 +12,16 @@
 // * one workgroup (4 waves) per (sequence, KV head, block of 256/G query rows);
 //   the G query heads of the KV head are packed into 256 rows, 64 per wave, so
 //   every K/V tile staged in LDS serves all G heads;
-// * K/V tiles of 64 keys are copied from the pool to LDS in the pool's own
-//   16-byte layout (double-buffered through registers): K as [D/8][64][8],
-//   V as [8][D][8] (8 consecutive keys of one head-dim index per 16 bytes);
+// * K/V tiles of 64 keys are copied from the pool to LDS (double-buffered
+//   through registers): K in the pool's own layout [D/8][64][8], V as
+//   [4 steps][D][2 halves][8 keys];
 // * S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T from registers (loaded
 //   once), so each lane owns one query column and its softmax statistics;
 // * the row max needs one exchange with lane l^32; the weights P^T come out of
 //   the accumulator already in the B-operand layout of the next product;
-// * O^T += V^T P^T: A = V^T from LDS (two 8-byte reads per fragment because the
-//   accumulator's key order is {4h..4h+3, 8+4h..8+4h+3} per lane half h).
+// * O^T += V^T P^T: A = V^T from LDS. The accumulator hands lane half h the keys
+//   {4h..4h+3, 8+4h..8+4h+3} of each 16-key step, so V is staged in LDS with its
+//   keys in that order and every A fragment is one 16-byte read.
 #include <math.h>
 
 #include "pa_device.h"
@@ -57,6 +58,7 @@ struct PrefillArgs {
   int block_size;
   int max_seqlen_q;
   int cap_k;
+  int block_shift;  // log2(block_size)
   int num_qblocks;
   float scale_log2;
 };
@@ -97,7 +99,7 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kVLoads = (kBN / 8) * kD / kPrefillThreads;
 
   __shared__ uint4 k_s[2][kKC][kBN];
-  __shared__ uint4 v_s[2][kBN / 8][kD];
+  __shared__ uint4 v_s[2][kBN / 16][kD][2];
 
   const int Hkv = a.num_kv_heads;
   const int bid = blockIdx.x;
@@ -157,50 +159,64 @@ void prefill_kernel(const PrefillArgs a) {
     for (int ks = 0; ks < kKS; ++ks) qf[nb][ks] = qp[ks * 2 + half];
   }
 
-  // ---- tile loader: pool -> registers -> LDS
+  // ---- tile loader: pool -> registers -> LDS.
+  // K: thread t always loads key (t % 64) of the tile, chunks t/64 + 4u: one
+  // block-table lookup per tile. V: thread t loads head-dim index t % D of the
+  // tile's 8-key chunks. Block sizes are powers of two (shift/mask).
+  // LDS V layout per 16-key step s: [d][h][16 bytes] holding keys
+  // {4h..4h+3} and {8+4h..8+4h+3} of the step, the order in which the P^T
+  // accumulator hands keys to lane half h, so an A fragment is one 16-byte read.
+  const int bshift = a.block_shift;
+  const int bmask = bs - 1;
+  const int k_key = tid % kBN;            // K: this thread's key within the tile
+  const int k_c0 = tid / kBN;             // K: first chunk (then + 4u)
+  const int v_d = tid % kD;               // V: head-dim index
+  const int v_j0 = tid / kD;              // V: first 8-key chunk (then + kPrefillThreads/kD * u)
   uint4 kreg[kKLoads], vreg[kVLoads];
   auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < kKLoads; ++u) {
-      const int idx = u * kPrefillThreads + tid;
-      const int c = idx / kBN;
-      const int key = kt * kBN + idx % kBN;
+    const int key0 = kt * kBN;
+    const bool tail = key0 + kBN > Lk;    // only the last tile reaches past Lk
+    {
+      const int key = key0 + k_key;
       const int kc = key < Lk ? key : Lk - 1;
-      const uint4* src = kpool + bt[kc / bs] * blk16 + (long long)c * bs + kc % bs;
-      uint4 v = *src;
-      if (key >= Lk) v = make_uint4(0u, 0u, 0u, 0u);
-      kreg[u] = v;
+      const uint4* src = kpool + bt[kc >> bshift] * blk16 + (kc & bmask);
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u) {
+        uint4 v = src[(long long)(k_c0 + u * (kPrefillThreads / kBN)) << bshift];
+        if (tail && key >= Lk) v = make_uint4(0u, 0u, 0u, 0u);
+        kreg[u] = v;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      const int idx = u * kPrefillThreads + tid;
-      const int j = idx / kD;       // 8-key chunk of the tile
-      const int d = idx % kD;
-      const int key = kt * kBN + j * 8;
+      const int j = v_j0 + u * (kPrefillThreads / kD);   // 8-key chunk of the tile
+      const int key = key0 + j * 8;
       const int kc = key < Lk ? key : ((Lk - 1) & ~7);
-      const uint4* src = vpool + bt[kc / bs] * blk16 + (long long)((kc % bs) / 8) * kD + d;
-      uint4 v = *src;
-      const int nv = Lk - key;      // valid keys in this chunk
-      if (nv < 8) {
-        uint32_t e[4] = {v.x, v.y, v.z, v.w};
+      uint4 v = vpool[bt[kc >> bshift] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
+      if (tail) {
+        const int nv = Lk - key;          // valid keys in this chunk
+        if (nv < 8) {
+          uint32_t e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          e[i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
-        v = make_uint4(e[0], e[1], e[2], e[3]);
+          for (int i = 0; i < 4; ++i)
+            e[i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+          v = make_uint4(e[0], e[1], e[2], e[3]);
+        }
       }
       vreg[u] = v;
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < kKLoads; ++u) {
-      const int idx = u * kPrefillThreads + tid;
-      k_s[buf][idx / kBN][idx % kBN] = kreg[u];
-    }
+    for (int u = 0; u < kKLoads; ++u) k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = kreg[u];
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      const int idx = u * kPrefillThreads + tid;
-      v_s[buf][idx / kD][idx % kD] = vreg[u];
+      const int j = v_j0 + u * (kPrefillThreads / kD);
+      const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
+      // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
+      uint2* dst = reinterpret_cast<uint2*>(&v_s[buf][step][v_d][0]);
+      dst[0 * 2 + second] = make_uint2(vreg[u].x, vreg[u].y);
+      dst[1 * 2 + second] = make_uint2(vreg[u].z, vreg[u].w);
     }
   };
 
@@ -312,11 +328,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const int d = db * 32 + l32;
-          const uint2* c0 = reinterpret_cast<const uint2*>(&v_s[buf][2 * t][d]);
-          const uint2* c1 = reinterpret_cast<const uint2*>(&v_s[buf][2 * t + 1][d]);
-          const uint2 lo = c0[half];
-          const uint2 hi = c1[half];
-          const bf16x8_t af = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          const bf16x8_t af = as_bf16x8(v_s[buf][t][d][half]);
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb)
             o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
@@ -383,6 +395,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool.num_kv_heads;
   a.block_size = pool.block_size;
+  a.block_shift = __builtin_ctz(unsigned(pool.block_size));
   a.max_seqlen_q = max_seqlen_q;
   a.cap_k = max_seqlen_k;
   a.num_qblocks = (max_seqlen_q + bm - 1) / bm;
