@@ -173,13 +173,26 @@ void prefill_kernel(const PrefillArgs a) {
   const int v_d = tid % kD;               // V: head-dim index
   const int v_j0 = tid / kD;              // V: first 8-key chunk (then + kPrefillThreads/kD * u)
   uint4 kreg[kKLoads], vreg[kVLoads];
-  auto load_tile = [&](int kt) {
+  // block ids are fetched one tile before the loads that use them, so the
+  // K/V loads never wait on a dependent block-table read
+  struct TileIds { int k; int v[kVLoads]; };
+  auto fetch_ids = [&](int kt, TileIds& ids) {
+    const int key0 = kt * kBN;
+    const int key = key0 + k_key;
+    ids.k = bt[(key < Lk ? key : Lk - 1) >> bshift];
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) {
+      const int vkey = key0 + (v_j0 + u * (kPrefillThreads / kD)) * 8;
+      ids.v[u] = bt[(vkey < Lk ? vkey : Lk - 1) >> bshift];
+    }
+  };
+  auto load_tile = [&](int kt, const TileIds& ids) {
     const int key0 = kt * kBN;
     const bool tail = key0 + kBN > Lk;    // only the last tile reaches past Lk
     {
       const int key = key0 + k_key;
       const int kc = key < Lk ? key : Lk - 1;
-      const uint4* src = kpool + bt[kc >> bshift] * blk16 + (kc & bmask);
+      const uint4* src = kpool + ids.k * blk16 + (kc & bmask);
 #pragma unroll
       for (int u = 0; u < kKLoads; ++u) {
         uint4 v = src[(long long)(k_c0 + u * (kPrefillThreads / kBN)) << bshift];
@@ -192,7 +205,7 @@ void prefill_kernel(const PrefillArgs a) {
       const int j = v_j0 + u * (kPrefillThreads / kD);   // 8-key chunk of the tile
       const int key = key0 + j * 8;
       const int kc = key < Lk ? key : ((Lk - 1) & ~7);
-      uint4 v = vpool[bt[kc >> bshift] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
+      uint4 v = vpool[ids.v[u] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
       if (tail) {
         const int nv = Lk - key;          // valid keys in this chunk
         if (nv < 8) {
@@ -233,14 +246,18 @@ void prefill_kernel(const PrefillArgs a) {
   }
   const float sc = a.scale_log2;
 
+  TileIds ids;
   if (ntiles > 0) {
-    load_tile(0);
+    fetch_ids(0, ids);
+    load_tile(0, ids);
+    if (ntiles > 1) fetch_ids(1, ids);
     store_tile(0);
   }
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (kt + 1 < ntiles) load_tile(kt + 1, ids);
+    if (kt + 2 < ntiles) fetch_ids(kt + 2, ids);
     const int key0 = kt * kBN;
     if (key0 <= wave_last) {
       // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
