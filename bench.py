@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_TBS = 8.0              # MI355X HBM3E, TB/s
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -89,6 +90,25 @@ def prefill_work(w):
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     byts = kv + 2 * tq * w.num_q_heads * w.head_dim * 2 + 4 * entries + 8 * (len(cu_q))
     return flops, byts
+
+
+def decode_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the decode sources changed since it was taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "decode_source_sha256: ")))
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pa_device.h", "pa_launch.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("decode_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 # ---------------------------------------------------------------- GPU set-up
@@ -304,9 +324,12 @@ def main():
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
                                    f"mean {float(w.context_lens.mean()):.1f}",
                    "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (decode + LSE reduce)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_kernel (pa_decode; contexts whole, no reduce)" if r["P"] >= w.max_context_len
+                     else "decode_kernel + decode_reduce_kernel (pa_decode)",
                      "achieved": round(dec_tbs * 1e3, 2), "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
-                     "frac": round(dec_tbs / HBM_PEAK_TBS, 4), "traffic": None,
+                     "frac": round(dec_tbs / HBM_PEAK_TBS, 4),
+                     "traffic": decode_traffic() if args.workload == 2 and args.partition_size is None else None,
                      "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
         "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
     }
