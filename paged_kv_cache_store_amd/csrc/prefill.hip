@@ -172,7 +172,9 @@ void prefill_kernel(const PrefillArgs a) {
   const int k_c0 = tid / kBN;             // K: first chunk (then + 4u)
   const int v_d = tid % kD;               // V: head-dim index
   const int v_j0 = tid / kD;              // V: first 8-key chunk (then + kPrefillThreads/kD * u)
-  uint4 kreg[kKLoads], vreg[kVLoads];
+  // staging registers use a native vector type: with HIP's union-based uint4 the
+  // array is not split into registers and the backend moves it into LDS
+  u32x4_t kreg[kKLoads], vreg[kVLoads];
   // block ids are fetched one tile before the loads that use them, so the
   // K/V loads never wait on a dependent block-table read
   struct TileIds { int k; int v[kVLoads]; };
@@ -188,48 +190,48 @@ void prefill_kernel(const PrefillArgs a) {
   };
   auto load_tile = [&](int kt, const TileIds& ids) {
     const int key0 = kt * kBN;
-    const bool tail = key0 + kBN > Lk;    // only the last tile reaches past Lk
     {
       const int key = key0 + k_key;
       const int kc = key < Lk ? key : Lk - 1;
       const uint4* src = kpool + ids.k * blk16 + (kc & bmask);
+      // keys past Lk read the last key instead; their scores are masked
 #pragma unroll
-      for (int u = 0; u < kKLoads; ++u) {
-        uint4 v = src[(long long)(k_c0 + u * (kPrefillThreads / kBN)) << bshift];
-        if (tail && key >= Lk) v = make_uint4(0u, 0u, 0u, 0u);
-        kreg[u] = v;
-      }
+      for (int u = 0; u < kKLoads; ++u)
+        kreg[u] = reinterpret_cast<const u32x4_t*>(src)[(long long)(k_c0 + u * (kPrefillThreads / kBN)) << bshift];
     }
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
       const int j = v_j0 + u * (kPrefillThreads / kD);   // 8-key chunk of the tile
       const int key = key0 + j * 8;
       const int kc = key < Lk ? key : ((Lk - 1) & ~7);
-      uint4 v = vpool[ids.v[u] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
-      if (tail) {
-        const int nv = Lk - key;          // valid keys in this chunk
-        if (nv < 8) {
-          uint32_t e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            e[i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
-          v = make_uint4(e[0], e[1], e[2], e[3]);
-        }
-      }
-      vreg[u] = v;
+      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[u] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
     }
   };
-  auto store_tile = [&](int buf) {
+  // V values past Lk are zeroed here, where the loads have landed anyway (their
+  // weights are 0, but a stale or NaN value would still poison 0 * v)
+  auto store_tile = [&](int buf, int kt) {
 #pragma unroll
-    for (int u = 0; u < kKLoads; ++u) k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = kreg[u];
+    for (int u = 0; u < kKLoads; ++u)
+      k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = __builtin_bit_cast(uint4, kreg[u]);
+    if (kt * kBN + kBN > Lk) {
+#pragma unroll
+      for (int u = 0; u < kVLoads; ++u) {
+        const int nv = Lk - (kt * kBN + (v_j0 + u * (kPrefillThreads / kD)) * 8);  // valid keys of the chunk
+        if (nv < 8) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vreg[u][i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
       const int j = v_j0 + u * (kPrefillThreads / kD);
       const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
       // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
       uint2* dst = reinterpret_cast<uint2*>(&v_s[buf][step][v_d][0]);
-      dst[0 * 2 + second] = make_uint2(vreg[u].x, vreg[u].y);
-      dst[1 * 2 + second] = make_uint2(vreg[u].z, vreg[u].w);
+      dst[0 * 2 + second] = make_uint2(vreg[u][0], vreg[u][1]);
+      dst[1 * 2 + second] = make_uint2(vreg[u][2], vreg[u][3]);
     }
   };
 
@@ -246,18 +248,24 @@ void prefill_kernel(const PrefillArgs a) {
   }
   const float sc = a.scale_log2;
 
+  // Software pipeline over 64-key tiles: tile kt+1 sits in registers while tile
+  // kt is computed from LDS; after the products it is written to the other LDS
+  // buffer and the loads of tile kt+2 are issued, so every load has a whole
+  // iteration to land before its LDS write (block ids one iteration earlier).
   TileIds ids;
   if (ntiles > 0) {
     fetch_ids(0, ids);
     load_tile(0, ids);
-    if (ntiles > 1) fetch_ids(1, ids);
-    store_tile(0);
+    store_tile(0, 0);
+    if (ntiles > 1) {
+      fetch_ids(1, ids);
+      load_tile(1, ids);
+    }
+    if (ntiles > 2) fetch_ids(2, ids);
   }
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < ntiles) load_tile(kt + 1, ids);
-    if (kt + 2 < ntiles) fetch_ids(kt + 2, ids);
     const int key0 = kt * kBN;
     if (key0 <= wave_last) {
       // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
@@ -353,7 +361,9 @@ void prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1);
+    if (kt + 1 < ntiles) store_tile(buf ^ 1, kt + 1);
+    if (kt + 2 < ntiles) load_tile(kt + 2, ids);
+    if (kt + 3 < ntiles) fetch_ids(kt + 3, ids);
     __syncthreads();
   }
 
