@@ -8,6 +8,8 @@ A step is one pass of the path over one synthetic batch, all on one stream:
   * the mixed chunked-prefill step (--workload 4): pa_store_kv of 4344 new
     tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
     of 248 sequences.
+The step's calls are captured once as a HIP graph and replayed (--eager times
+them as separate calls; both figures are in the line).
 Inputs are resident in HBM before the timed region. `value` is the step's
 algorithmic bytes (unique KV bytes read by decode and prefill, q/out, tables,
 plus the store's reads and writes) divided by the wall time per step. The
@@ -174,8 +176,11 @@ class Setup:
                                w.max_seqlen_q, w.max_seqlen_k, out=self.pout)
 
 
-def run_steps(st, steps, warmup):
-    """Warm up, then time `steps` steps; per-call HIP events on the launch stream."""
+def run_steps(st, steps, warmup, graph=True):
+    """Warm up; time `steps` eager steps with HIP events around each call (on the
+    stream the library launches on); then, with graph=True, capture one step as a
+    HIP graph and time `steps` replays between two synchronisations.
+    Returns (ms per step, per-call ms, ms per eager step)."""
     torch = st.torch
     calls = [("store", st.store)]
     if st.w.has_prefill:
@@ -203,7 +208,24 @@ def run_steps(st, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
-    return (t1 - t0) * 1e3 / steps, ms
+    ms_eager = (t1 - t0) * 1e3 / steps
+    if not graph:
+        return ms_eager, ms, ms_eager
+
+    def step():
+        for _, f in calls:
+            f()
+
+    g = st.pa.capture_step(step)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, ms, ms_eager
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -275,6 +297,8 @@ def main():
                     help="decode partition size (default: the workload's, else automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step as individual calls instead of one HIP-graph replay")
     ap.add_argument("--copy-calib", action="store_true",
                     help="time a plain 1 GiB device copy (counter calibration / HBM ceiling) and exit")
     args = ap.parse_args()
@@ -297,9 +321,9 @@ def main():
         if args.partition_size is not None:
             w.partition_size = args.partition_size
         st = Setup(w)
-        ms_step, ms = run_steps(st, steps, warmup)
+        ms_step, ms, ms_eager = run_steps(st, steps, warmup, graph=not args.eager)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
-        res = {"w": w, "ms_step": ms_step, "ms": ms, "decode_bytes": dec_b,
+        res = {"w": w, "ms_step": ms_step, "ms_eager": ms_eager, "ms": ms, "decode_bytes": dec_b,
                "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P}
         if w.has_prefill:
             res["prefill_flops"], res["prefill_bytes"] = prefill_work(w)
@@ -323,7 +347,8 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
                                    f"mean {float(w.context_lens.mean()):.1f}",
-                   "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU"},
+                   "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU",
+                   "launch": "eager calls" if args.eager else "one HIP-graph replay per step"},
         "roofline": {"bound": "hbm",
                      "kernel": "decode_kernel (pa_decode; contexts whole, no reduce)" if r["P"] >= w.max_context_len
                      else "decode_kernel + decode_reduce_kernel (pa_decode)",
@@ -332,6 +357,7 @@ def main():
                      "traffic": decode_traffic() if args.workload == 2 and args.partition_size is None else None,
                      "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
         "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
+        "ms_per_step_eager": round(r["ms_eager"], 5),
     }
     if not args.no_extra:
         extra = {}

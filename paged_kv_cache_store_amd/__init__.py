@@ -17,7 +17,7 @@ import re
 import torch
 
 __all__ = ["store_kv", "decode", "prefill_varlen", "decode_workspace_size",
-           "decode_partition_size", "empty_pools", "PaError", "LIB_PATH", "library"]
+           "decode_partition_size", "empty_pools", "capture_step", "PaError", "LIB_PATH", "library"]
 
 # PA_LIBRARY may point at another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -216,6 +216,27 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
     if st != 0:
         raise PaError(st, "pa_prefill_varlen")
     return out
+
+
+def capture_step(fn, warmup=1):
+    """Record the library calls made by fn() once as a HIP graph and return it;
+    graph.replay() then re-issues the same kernels with the same arguments and
+    no per-call host work. Every buffer fn() touches (pools, tables, outputs,
+    decode workspace) must be allocated before the call and kept alive while the
+    graph is used; nothing is allocated during capture. The library enqueues no
+    memset and no host synchronisation, so its calls are capturable. CUDA-graph
+    replay of a fixed kernel sequence is the launch-overhead removal the pages
+    describe ("Nano-vLLM：轻量高效的大模型推理框架…", 三.2 (3) CUDA图与Torch编译)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
 
 
 def header_functions(header_path=None):
