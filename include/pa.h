@@ -61,7 +61,9 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* sizes are negative or inconsistent                   */
   PA_ERR_UNSUPPORTED = -3, /* head_dim, block_size, group size or dtype not built  */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required           */
-  PA_ERR_HIP = -5          /* a HIP call failed; see pa_last_hip_error()            */
+  PA_ERR_HIP = -5,         /* a HIP call failed; see pa_last_hip_error()            */
+  PA_ERR_NO_BLOCKS = -6,   /* block manager: the pool cannot hold the request        */
+  PA_ERR_NOT_FOUND = -7    /* block manager: unknown sequence id                     */
 } pa_status;
 
 typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;

@@ -17,7 +17,8 @@ import re
 import torch
 
 __all__ = ["store_kv", "decode", "prefill_varlen", "decode_workspace_size",
-           "decode_partition_size", "empty_pools", "capture_step", "PaError", "LIB_PATH", "library"]
+           "decode_partition_size", "empty_pools", "capture_step", "copy_blocks", "BlockManager",
+           "PaError", "LIB_PATH", "library"]
 
 # PA_LIBRARY may point at another build of the same library (e.g. a tuning variant)
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -56,6 +57,26 @@ def _load():
     lib.pa_decode.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
     lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
     for name in ("pa_store_kv", "pa_decode", "pa_prefill_varlen"):
+        getattr(lib, name).restype = ctypes.c_int
+    I64, PI32, PI64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_bm_create.argtypes = [I32, I32, I32, ctypes.POINTER(P)]
+    lib.pa_bm_destroy.argtypes = [P]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_num_free_blocks.argtypes = [P]
+    lib.pa_bm_num_free_blocks.restype = I32
+    lib.pa_bm_add_sequence.argtypes = [P, PI32, I32, PI64, PI32]
+    lib.pa_bm_append_token.argtypes = [P, I64, I32, PI32, PI32, PI32]
+    lib.pa_bm_fork.argtypes = [P, I64, PI64]
+    lib.pa_bm_free_sequence.argtypes = [P, I64]
+    lib.pa_bm_sequence_info.argtypes = [P, I64, PI32, PI32]
+    lib.pa_bm_block_table.argtypes = [P, I64, PI32, I32, I32]
+    lib.pa_bm_slots.argtypes = [P, I64, I32, I32, PI32]
+    lib.pa_bm_block_refcount.argtypes = [P, I32]
+    lib.pa_bm_block_refcount.restype = I32
+    for name in ("pa_bm_create", "pa_bm_add_sequence", "pa_bm_append_token", "pa_bm_fork",
+                 "pa_bm_free_sequence", "pa_bm_sequence_info", "pa_bm_block_table", "pa_bm_slots"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -99,7 +120,7 @@ def _check(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} must be a GPU tensor")
 
 
-def _pool_desc(k_cache, v_cache, k_scale, v_scale):
+def _pool_desc(k_cache, v_cache, k_scale, v_scale, need_scales=True):
     if k_cache.dtype == torch.bfloat16:
         dtype, x = PA_KV_BF16, 8
     elif k_cache.dtype == torch.uint8:
@@ -112,7 +133,10 @@ def _pool_desc(k_cache, v_cache, k_scale, v_scale):
     if xx != x or tuple(v_cache.shape) != (nb, hkv, bs // x, dx * x, x) or bs % x:
         raise ValueError(f"pool shapes {tuple(k_cache.shape)} / {tuple(v_cache.shape)} "
                          f"do not match the layout for x={x}")
-    if dtype == PA_KV_FP8_E4M3:
+    if dtype == PA_KV_FP8_E4M3 and not need_scales:
+        # calls that only move bytes: the C ABI still wants non-NULL scale pointers
+        k_scale = v_scale = k_cache
+    elif dtype == PA_KV_FP8_E4M3:
         for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
             if sc is None:
                 raise ValueError(f"{name} is required for an fp8 pool")
@@ -239,10 +263,93 @@ def capture_step(fn, warmup=1):
     return graph
 
 
-def header_functions(header_path=None):
-    """Names of the functions include/pa.h declares."""
+def copy_blocks(k_cache, v_cache, pairs, stream=None):
+    """Copy whole blocks inside the pools; pairs: device int32 [n, 2] of (src, dst)."""
+    desc, *_ = _pool_desc(k_cache, v_cache, None, None, need_scales=False)
+    _check(pairs, "pairs", torch.int32, 2, k_cache.device)
+    st = library().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(pairs), pairs.shape[0],
+                                  ctypes.byref(desc), _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_copy_blocks")
+
+
+class BlockManager:
+    """Host-side block manager with prefix caching (C++ in libpa; see
+    include/pa_block_manager.h). Hands out the blocks of one pool, returns the
+    block tables and slot mappings the kernels consume."""
+
+    def __init__(self, num_blocks, block_size, prefix_caching=True):
+        self._lib = library()
+        h = ctypes.c_void_p()
+        st = self._lib.pa_bm_create(num_blocks, block_size, 1 if prefix_caching else 0, ctypes.byref(h))
+        if st != 0:
+            raise PaError(st, "pa_bm_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pa_bm_destroy(h)
+            self._h = None
+
+    def _call(self, name, *args):
+        st = getattr(self._lib, name)(self._h, *args)
+        if st != 0:
+            raise PaError(st, name)
+
+    @property
+    def num_free_blocks(self):
+        return int(self._lib.pa_bm_num_free_blocks(self._h))
+
+    def add_sequence(self, tokens):
+        """Returns (seq_id, num_cached_tokens)."""
+        arr = (ctypes.c_int32 * max(1, len(tokens)))(*tokens)
+        sid, cached = ctypes.c_int64(), ctypes.c_int32()
+        self._call("pa_bm_add_sequence", arr, len(tokens), ctypes.byref(sid), ctypes.byref(cached))
+        return sid.value, cached.value
+
+    def append_token(self, seq_id, token):
+        """Returns (slot, (cow_src, cow_dst) or None)."""
+        slot, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._call("pa_bm_append_token", seq_id, token, ctypes.byref(slot), ctypes.byref(src), ctypes.byref(dst))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def fork(self, seq_id):
+        new = ctypes.c_int64()
+        self._call("pa_bm_fork", seq_id, ctypes.byref(new))
+        return new.value
+
+    def free(self, seq_id):
+        self._call("pa_bm_free_sequence", seq_id)
+
+    def info(self, seq_id):
+        """Returns (num_tokens, num_blocks)."""
+        n, b = ctypes.c_int32(), ctypes.c_int32()
+        self._call("pa_bm_sequence_info", seq_id, ctypes.byref(n), ctypes.byref(b))
+        return n.value, b.value
+
+    def block_table(self, seq_id, max_blocks, pad_block=0):
+        row = (ctypes.c_int32 * max(1, max_blocks))()
+        self._call("pa_bm_block_table", seq_id, row, max_blocks, pad_block)
+        return list(row)[:max_blocks]
+
+    def slots(self, seq_id, first_pos, count):
+        out = (ctypes.c_int32 * max(1, count))()
+        self._call("pa_bm_slots", seq_id, first_pos, count, out)
+        return list(out)[:count]
+
+    def refcount(self, block):
+        return int(self._lib.pa_bm_block_refcount(self._h, block))
+
+
+def header_functions(header_dir=None):
+    """Names of the functions the headers in include/ declare."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = header_path or os.path.join(os.path.dirname(here), "include", "pa.h")
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    inc = header_dir or os.path.join(os.path.dirname(here), "include")
+    names = set()
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, f)).read(), flags=re.S)
+            names.update(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = [
@@ -48,7 +48,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
         objs = []
         for src in SOURCES:
-            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            obj = os.path.join(tmp, src.rsplit(".", 1)[0] + ".o")
             cmd = [HIPCC, *DEVICE_FLAGS, *["-D" + d for d in defines], "-I", INCLUDE, "-I", CSRC, "-c",
                    os.path.join(CSRC, src), "-o", obj]
             if verbose:

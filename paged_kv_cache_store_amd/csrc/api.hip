@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "pa.h"
+#include "pa_block_manager.h"
 #include "pa_launch.h"
 
 namespace {
@@ -66,6 +67,8 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or dtype not supported";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP error (see pa_last_hip_error)";
+    case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PA_ERR_NOT_FOUND: return "unknown sequence id";
   }
   return "unknown status";
 }
@@ -86,6 +89,18 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
                                         slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
                                         static_cast<uint8_t*>(v_cache), dims, cache->k_scale,
                                         cache->v_scale, stream));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                         const pa_cache_desc* cache, hipStream_t stream) {
+  pa::PoolDims dims;
+  pa_status st = check_cache(cache, &dims);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0 || num_pairs > 65535) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
+  return hip_status(pa::launch_copy_blocks(static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
+                                           pairs, num_pairs, dims, stream));
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,

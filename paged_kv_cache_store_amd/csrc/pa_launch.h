@@ -17,6 +17,9 @@ hipError_t launch_store_kv(const uint16_t* k, const uint16_t* v, const int32_t* 
                            const PoolDims& pool, const float* k_scale, const float* v_scale,
                            hipStream_t stream);
 
+hipError_t launch_copy_blocks(uint8_t* k_cache, uint8_t* v_cache, const int32_t* pairs, int num_pairs,
+                              const PoolDims& pool, hipStream_t stream);
+
 // Workspace layout for a decode with num_parts partitions per sequence:
 //   float o[num_seqs][num_q_heads][num_parts][head_dim]   (unnormalised partial output)
 //   float m[num_seqs][num_q_heads][num_parts]              (partial max, log2 units)

@@ -95,3 +95,34 @@ hipError_t launch_store_kv(const uint16_t* k, const uint16_t* v, const int32_t* 
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// Copy-on-write support: copies whole blocks (all KV heads, K then V) inside a
+// pool. Thread = one 16-byte unit of a block's K or V; pairs[i] = {src, dst}.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          long long block16) {
+  const int p = blockIdx.y;
+  const long long src = pairs[2 * p], dst = pairs[2 * p + 1];
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < 2 * block16;
+       i += (long long)gridDim.x * blockDim.x) {
+    uint4* pool = i < block16 ? k_cache : v_cache;
+    const long long j = i < block16 ? i : i - block16;
+    pool[dst * block16 + j] = pool[src * block16 + j];
+  }
+}
+
+hipError_t launch_copy_blocks(uint8_t* k_cache, uint8_t* v_cache, const int32_t* pairs, int num_pairs,
+                              const PoolDims& pool, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const long long block16 =
+      (long long)pool.num_kv_heads * pool.block_size * pool.head_dim * (pool.fp8 ? 1 : 2) / 16;
+  const unsigned gx = unsigned((2 * block16 + 255) / 256 < 64 ? (2 * block16 + 255) / 256 : 64);
+  copy_blocks_kernel<<<dim3(gx, unsigned(num_pairs)), 256, 0, stream>>>(
+      reinterpret_cast<uint4*>(k_cache), reinterpret_cast<uint4*>(v_cache), pairs, block16);
+  return hipGetLastError();
+}
+
+}  // namespace pa

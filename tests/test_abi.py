@@ -22,14 +22,15 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = pa.header_functions()
-    assert set(names) == {"pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_decode_workspace_size",
-                          "pa_decode_partition_size", "pa_status_string", "pa_last_hip_error"}
+    assert {"pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_decode_workspace_size",
+            "pa_decode_partition_size", "pa_status_string", "pa_last_hip_error", "pa_copy_blocks",
+            "pa_bm_create", "pa_bm_add_sequence", "pa_bm_append_token"} <= set(names)
     for n in names:
         assert getattr(lib, n) is not None
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, 7):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, 7):
         assert lib.pa_status_string(s)
     assert lib.pa_last_hip_error() == b""
 

@@ -335,3 +335,40 @@ def custom(*, seed=7, Hq=4, Hkv=2, D=64, bs=16, context_lens=(1, 5, 33), prefill
                   prefill=prefill, kv_dtype=kv_dtype, partition_size=partition_size,
                   sharers=sharers, shared_prefix_blocks=shared_prefix_blocks,
                   num_blocks=num_blocks)
+
+
+def _prefix_digest(tokens) -> list:
+    """64-bit digest of every prefix tokens[:p+1] (for seeding per-position draws)."""
+    out = []
+    h = 1469598103934665603
+    for t in tokens:
+        h ^= (int(t) & 0xFFFFFFFF) + 0x9E3779B97F4A7C15
+        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+        h ^= h >> 29
+        out.append(h)
+    return out
+
+
+def prefix_kv(tokens, num_kv_heads: int, head_dim: int, seed: int = 77):
+    """bf16 K and V rows [len(tokens), Hkv, D] where position p's values depend
+    only on tokens[:p+1]: sequences with equal prefixes get equal K/V there, as a
+    model's KV cache does (what prefix caching relies on)."""
+    d = _prefix_digest(tokens)
+    K = np.empty((len(tokens), num_kv_heads, head_dim), np.uint16)
+    V = np.empty_like(K)
+    for p, h in enumerate(d):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, h & 0xFFFFFFFF, h >> 32]))
+        x = rng.standard_normal((2, num_kv_heads, head_dim), dtype=np.float32)
+        K[p] = f32_to_bf16_bits(x[0])
+        V[p] = f32_to_bf16_bits(x[1])
+    return K, V
+
+
+def prefix_q(tokens, num_q_heads: int, head_dim: int, seed: int = 78):
+    """bf16 query rows [len(tokens), Hq, D], position p's depending on tokens[:p+1]."""
+    d = _prefix_digest(tokens)
+    Q = np.empty((len(tokens), num_q_heads, head_dim), np.uint16)
+    for p, h in enumerate(d):
+        rng = np.random.default_rng(np.random.SeedSequence([seed, h & 0xFFFFFFFF, h >> 32]))
+        Q[p] = f32_to_bf16_bits(rng.standard_normal((num_q_heads, head_dim), dtype=np.float32))
+    return Q
