@@ -173,7 +173,8 @@ class Setup:
     def prefill(self):
         w = self.w
         self.pa.prefill_varlen(self.pq, self.kc, self.vc, self.cu_q, self.cu_k, self.pbt, float(w.scale),
-                               w.max_seqlen_q, w.max_seqlen_k, out=self.pout)
+                               w.max_seqlen_q, w.max_seqlen_k, out=self.pout, k_scale=self.ks,
+                               v_scale=self.vs)
 
 
 def run_steps(st, steps, warmup, graph=True):
@@ -292,7 +293,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--partition-size", type=int, default=None,
                     help="decode partition size (default: the workload's, else automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -361,7 +362,7 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for number in [n for n in (3, 4, 5) if n != args.workload]:
+        for number in [n for n in (3, 4, 5, 6) if n != args.workload]:
             log(f"[bench] workload {number}")
             e = measure(number, max(5, args.steps // 2), 2)
             ent = {"decode_TBps": round(e["decode_bytes"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),

@@ -142,8 +142,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * pa_store_kv): chunked prefill ("nano-vllm-lite…", 核心技术改进 §2).
  *   q             device bf16 [total_q][num_q_heads][head_dim]; sequence s owns
  *                 rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
- *   k_cache, v_cache  the paged pools (bf16 only; fp8 pools return
- *                 PA_ERR_UNSUPPORTED)
+ *   k_cache, v_cache  the paged pools, bf16 or fp8 (an fp8 pool is read through
+ *                 cache->k_scale / v_scale exactly as pa_decode reads it: each
+ *                 E4M3 byte widened to bf16 without rounding, k_scale[h] folded
+ *                 into the softmax scale, v_scale[h] into the output)
  *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs+1] prefix sums; sequence s
  *                 has Lq = cu_q[s+1]-cu_q[s] queries and Lk = cu_k[s+1]-cu_k[s]
  *                 keys at logical positions 0..Lk-1 of its block table

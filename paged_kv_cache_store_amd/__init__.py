@@ -219,9 +219,10 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
 
 
 def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, scale,
-                   max_seqlen_q, max_seqlen_k, out=None, stream=None):
-    """Causal varlen prefill over the paged pools; returns out ([Tq, Hq, D] bf16)."""
-    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, None, None)
+                   max_seqlen_q, max_seqlen_k, out=None, k_scale=None, v_scale=None, stream=None):
+    """Causal varlen prefill over the paged pools; returns out ([Tq, Hq, D] bf16).
+    fp8 pools need k_scale / v_scale (device float32 [num_kv_heads])."""
+    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
     dev = k_cache.device
     _check(q, "q", torch.bfloat16, 3, dev)
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)

@@ -159,7 +159,6 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
   pa::PoolDims dims;
   pa_status st = check_cache(cache, &dims);
   if (st != PA_OK) return st;
-  if (dims.fp8) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_q_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
       max_blocks_per_seq <= 0)
     return PA_ERR_SHAPE;
@@ -175,7 +174,7 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                                        static_cast<const uint8_t*>(v_cache), cu_seqlens_q, cu_seqlens_k,
                                        block_tables, max_blocks_per_seq, num_seqs, num_q_heads,
                                        max_seqlen_q, cap_k, scale, static_cast<uint16_t*>(out), dims,
-                                       stream));
+                                       cache->k_scale, cache->v_scale, stream));
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
                           const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_tables,
                           int max_blocks_per_seq, int num_seqs, int num_q_heads,
                           int max_seqlen_q, int max_seqlen_k, float scale, uint16_t* out,
-                          const PoolDims& pool, hipStream_t stream);
+                          const PoolDims& pool, const float* k_scale, const float* v_scale,
+                          hipStream_t stream);
 
 }  // namespace pa

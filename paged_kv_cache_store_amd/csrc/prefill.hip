@@ -50,6 +50,8 @@ struct PrefillArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* block_tables;
+  const float* k_scale;
+  const float* v_scale;
   uint16_t* out;
   int max_blocks_per_seq;
   int num_seqs;
@@ -84,7 +86,7 @@ static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
 // (query row, head) columns, i.e. 128 * kNB / G query rows of each of the G heads.
-template <int kD, int kG, int kNB>
+template <int kD, int kG, int kNB, bool kFp8>
 __global__ __launch_bounds__(kPrefillThreads)
 #if PA_PREFILL_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
@@ -94,9 +96,10 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kBM = kCols / kG;        // query rows per workgroup
   constexpr int kKS = kD / 16;           // k-steps of S^T = K Q^T
   constexpr int kDB = kD / 32;           // 32-row blocks of O^T
-  constexpr int kKC = kD / 8;            // 16-byte chunks per key
-  constexpr int kKLoads = kKC * kBN / kPrefillThreads;   // 16-byte K loads per thread per tile
-  constexpr int kVLoads = (kBN / 8) * kD / kPrefillThreads;
+  constexpr int kKC = kD / 8;            // 16-byte bf16 chunks per key (LDS layout)
+  constexpr int kX = kFp8 ? 16 : 8;      // elements per 16-byte chunk of the pool
+  constexpr int kKLoads = (kD / kX) * kBN / kPrefillThreads;   // 16-byte K loads per thread per tile
+  constexpr int kVLoads = (kBN / kX) * kD / kPrefillThreads;
 
   __shared__ uint4 k_s[2][kKC][kBN];
   __shared__ uint4 v_s[2][kBN / 16][kD][2];
@@ -123,7 +126,7 @@ void prefill_kernel(const PrefillArgs a) {
   if (row0 >= Lq || Lq <= 0) return;
   const int bs = a.block_size;
   const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq;
-  const long long slab16 = (long long)bs * kD * 2 / 16;
+  const long long slab16 = (long long)bs * kD * (kFp8 ? 1 : 2) / 16;
   const uint4* kpool = reinterpret_cast<const uint4*>(a.k_cache) + (long long)hk * slab16;
   const uint4* vpool = reinterpret_cast<const uint4*>(a.v_cache) + (long long)hk * slab16;
   const long long blk16 = (long long)Hkv * slab16;
@@ -171,7 +174,7 @@ void prefill_kernel(const PrefillArgs a) {
   const int k_key = tid % kBN;            // K: this thread's key within the tile
   const int k_c0 = tid / kBN;             // K: first chunk (then + 4u)
   const int v_d = tid % kD;               // V: head-dim index
-  const int v_j0 = tid / kD;              // V: first 8-key chunk (then + kPrefillThreads/kD * u)
+  const int v_j0 = tid / kD;              // V: first x-key chunk (then + kPrefillThreads/kD * u)
   // staging registers use a native vector type: with HIP's union-based uint4 the
   // array is not split into registers and the backend moves it into LDS
   u32x4_t kreg[kKLoads], vreg[kVLoads];
@@ -184,7 +187,7 @@ void prefill_kernel(const PrefillArgs a) {
     ids.k = bt[(key < Lk ? key : Lk - 1) >> bshift];
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      const int vkey = key0 + (v_j0 + u * (kPrefillThreads / kD)) * 8;
+      const int vkey = key0 + (v_j0 + u * (kPrefillThreads / kD)) * kX;
       ids.v[u] = bt[(vkey < Lk ? vkey : Lk - 1) >> bshift];
     }
   };
@@ -201,37 +204,77 @@ void prefill_kernel(const PrefillArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      const int j = v_j0 + u * (kPrefillThreads / kD);   // 8-key chunk of the tile
-      const int key = key0 + j * 8;
-      const int kc = key < Lk ? key : ((Lk - 1) & ~7);
-      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[u] * blk16 + (long long)((kc & bmask) >> 3) * kD + v_d];
+      const int j = v_j0 + u * (kPrefillThreads / kD);   // x-key chunk of the tile
+      const int key = key0 + j * kX;
+      const int kc = key < Lk ? key : ((Lk - 1) & ~(kX - 1));
+      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[u] * blk16 + (long long)((kc & bmask) / kX) * kD + v_d];
     }
   };
   // V values past Lk are zeroed here, where the loads have landed anyway (their
   // weights are 0, but a stale or NaN value would still poison 0 * v)
   auto store_tile = [&](int buf, int kt) {
+    if constexpr (!kFp8) {
 #pragma unroll
-    for (int u = 0; u < kKLoads; ++u)
-      k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = __builtin_bit_cast(uint4, kreg[u]);
-    if (kt * kBN + kBN > Lk) {
+      for (int u = 0; u < kKLoads; ++u)
+        k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = __builtin_bit_cast(uint4, kreg[u]);
+      if (kt * kBN + kBN > Lk) {
 #pragma unroll
-      for (int u = 0; u < kVLoads; ++u) {
-        const int nv = Lk - (kt * kBN + (v_j0 + u * (kPrefillThreads / kD)) * 8);  // valid keys of the chunk
-        if (nv < 8) {
+        for (int u = 0; u < kVLoads; ++u) {
+          const int nv = Lk - (kt * kBN + (v_j0 + u * (kPrefillThreads / kD)) * 8);  // valid keys of the chunk
+          if (nv < 8) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vreg[u][i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+            for (int i = 0; i < 4; ++i)
+              vreg[u][i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+          }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kVLoads; ++u) {
-      const int j = v_j0 + u * (kPrefillThreads / kD);
-      const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
-      // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
-      uint2* dst = reinterpret_cast<uint2*>(&v_s[buf][step][v_d][0]);
-      dst[0 * 2 + second] = make_uint2(vreg[u][0], vreg[u][1]);
-      dst[1 * 2 + second] = make_uint2(vreg[u][2], vreg[u][3]);
+      for (int u = 0; u < kVLoads; ++u) {
+        const int j = v_j0 + u * (kPrefillThreads / kD);
+        const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
+        // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
+        uint2* dst = reinterpret_cast<uint2*>(&v_s[buf][step][v_d][0]);
+        dst[0 * 2 + second] = make_uint2(vreg[u][0], vreg[u][1]);
+        dst[1 * 2 + second] = make_uint2(vreg[u][2], vreg[u][3]);
+      }
+    } else {
+      // fp8 pool: a 16-byte chunk holds 16 values; converted exactly to bf16 here
+      // (every e4m3 value is a bf16 value), into the same LDS layouts as bf16.
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u) {
+        const int c8 = k_c0 + u * (kPrefillThreads / kBN);   // head-dims 16*c8 .. 16*c8+15
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[2 * i] = fp8x2_to_bf16x2<false>(kreg[u][i]);
+          w[2 * i + 1] = fp8x2_to_bf16x2<true>(kreg[u][i]);
+        }
+        k_s[buf][2 * c8][k_key] = make_uint4(w[0], w[1], w[2], w[3]);
+        k_s[buf][2 * c8 + 1][k_key] = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+#pragma unroll
+      for (int u = 0; u < kVLoads; ++u) {
+        const int step = v_j0 + u * (kPrefillThreads / kD);  // 16-key chunk = one PV step
+        const int nv = Lk - (kt * kBN + step * 16);           // valid keys of the chunk
+        if (nv < 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mask |= (4 * i + b < nv) ? (0xffu << (8 * b)) : 0u;
+            vreg[u][i] &= mask;
+          }
+        }
+        // dword i holds keys 4i..4i+3: half 0 takes keys {0-3, 8-11}, half 1 {4-7, 12-15}
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[2 * i] = fp8x2_to_bf16x2<false>(vreg[u][i]);
+          w[2 * i + 1] = fp8x2_to_bf16x2<true>(vreg[u][i]);
+        }
+        v_s[buf][step][v_d][0] = make_uint4(w[0], w[1], w[4], w[5]);
+        v_s[buf][step][v_d][1] = make_uint4(w[2], w[3], w[6], w[7]);
+      }
     }
   };
 
@@ -246,7 +289,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][nb][i] = 0.f;
   }
-  const float sc = a.scale_log2;
+  const float sc = kFp8 ? a.scale_log2 * a.k_scale[hk] : a.scale_log2;
 
   // Software pipeline over 64-key tiles: tile kt+1 sits in registers while tile
   // kt is computed from LDS; after the products it is written to the other LDS
@@ -371,7 +414,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const float L = pair_sum(lsum[nb]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = L > 0.f ? (kFp8 ? a.v_scale[hk] : 1.f) / L : 0.f;
     if (qrow[nb] < Lq) {
       uint16_t* op = a.out + ((long long)(q0 + qrow[nb]) * a.num_q_heads + head[nb]) * kD;
 #pragma unroll
@@ -391,13 +434,13 @@ void prefill_kernel(const PrefillArgs a) {
 
 constexpr int kNBLaunch = PA_PREFILL_NB;
 
-template <int kD>
+template <int kD, bool kFp8>
 static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   switch (G) {
-    case 1: prefill_kernel<kD, 1, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 2: prefill_kernel<kD, 2, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 4: prefill_kernel<kD, 4, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 8: prefill_kernel<kD, 8, kNBLaunch><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 1: prefill_kernel<kD, 1, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 2: prefill_kernel<kD, 2, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 4: prefill_kernel<kD, 4, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 8: prefill_kernel<kD, 8, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
     default: return false;
   }
 }
@@ -406,7 +449,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
                           const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_tables,
                           int max_blocks_per_seq, int num_seqs, int num_q_heads,
                           int max_seqlen_q, int max_seqlen_k, float scale, uint16_t* out,
-                          const PoolDims& pool, hipStream_t stream) {
+                          const PoolDims& pool, const float* k_scale, const float* v_scale,
+                          hipStream_t stream) {
   const int G = num_q_heads / pool.num_kv_heads;
   const int bm = kPrefillWaves * 32 * kNBLaunch / G;
   PrefillArgs a;
@@ -416,6 +460,8 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
   a.cu_q = cu_q;
   a.cu_k = cu_k;
   a.block_tables = block_tables;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.out = out;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -429,8 +475,11 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
   a.scale_log2 = scale * kLog2e;
   const unsigned grid = unsigned((long long)num_seqs * a.num_qblocks * pool.num_kv_heads);
   if (grid == 0) return hipSuccess;
-  const bool ok = pool.head_dim == 64 ? launch_prefill_g<64>(G, a, grid, stream)
-                                      : launch_prefill_g<128>(G, a, grid, stream);
+  bool ok;
+  if (pool.head_dim == 64)
+    ok = pool.fp8 ? launch_prefill_g<64, true>(G, a, grid, stream) : launch_prefill_g<64, false>(G, a, grid, stream);
+  else
+    ok = pool.fp8 ? launch_prefill_g<128, true>(G, a, grid, stream) : launch_prefill_g<128, false>(G, a, grid, stream);
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }

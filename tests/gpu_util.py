@@ -73,4 +73,5 @@ class GpuCase:
         w = self.w
         return self.pa.prefill_varlen(self.pq, self.k_cache, self.v_cache, self.cu_q, self.cu_k,
                                       self.p_block_tables, float(w.scale), w.max_seqlen_q,
-                                      w.max_seqlen_k, out=out)
+                                      w.max_seqlen_k, out=out, k_scale=self.k_scale,
+                                      v_scale=self.v_scale)

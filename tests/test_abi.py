@@ -98,7 +98,8 @@ def test_prefill_validation(lib):
     assert prefill(lib, None) == NULL
     assert prefill(lib, desc(), q=None) == NULL
     assert prefill(lib, desc(), hq=5) == SHAPE
-    assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE)) == UNSUP      # fp8 prefill not built
+    assert prefill(lib, desc(dtype=1)) == NULL                         # fp8 needs scales
+    assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE), hq=5) == SHAPE
     assert prefill(lib, desc(), mq=-1) == SHAPE
     assert prefill(lib, desc(), S=0, q=None) == OK
     for bad in (0.0, -0.5, float("inf"), float("nan")):

@@ -1,6 +1,7 @@
 """GPU parity of pa_prefill_varlen (causal varlen chunked prefill over the paged
 cache, MFMA) against the CPU oracle, plus invariants. Tolerance: element-wise
-|gpu - oracle| <= 1e-2 + 1e-2*|oracle| (bf16 cache, float32 accumulation)."""
+|gpu - oracle| <= 1e-2 + 1e-2*|oracle| for a bf16 cache, 3e-2 for an fp8 cache
+(the oracle reads the same fp8 bytes; float32 accumulation on the GPU)."""
 import numpy as np
 import pytest
 import torch
@@ -13,11 +14,12 @@ from tests.util import assert_close, bf16_f64, oracle_pools, relabel_blocks
 pytestmark = pytest.mark.gpu
 
 TOL = (1e-2, 1e-2)
+TOL_FP8 = (3e-2, 3e-2)
 
 
 def _oracle_prefill(w, kc, vc, seqs=None):
     return oracle.attention.prefill(w.pq, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.p_block_tables,
-                                    w.scale, w.block_size, seqs=seqs)
+                                    w.scale, w.block_size, w.k_scale, w.v_scale, seqs=seqs)
 
 
 CASES = [
@@ -41,6 +43,41 @@ def test_prefill_small(cfg):
     print(f"max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
+FP8_CASES = [
+    dict(seed=321, Hq=4, Hkv=1, D=128, bs=16, prefill=[(0, 1), (0, 17), (0, 64), (0, 65), (16, 16)]),
+    dict(seed=322, Hq=8, Hkv=2, D=128, bs=64, prefill=[(100, 30), (37, 200), (0, 300)]),
+    dict(seed=323, Hq=16, Hkv=8, D=64, bs=32, prefill=[(5, 250), (0, 129), (300, 1)]),
+    dict(seed=324, Hq=8, Hkv=1, D=64, bs=256, prefill=[(0, 40), (700, 33), (64, 270)]),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_CASES, ids=[f"fp8case{i}" for i in range(len(FP8_CASES))])
+def test_prefill_fp8_small(cfg):
+    """fp8 (E4M3) cache with per-head scales: every row against the oracle on the same bytes."""
+    print(f"fp8 case {cfg}", flush=True)
+    w = W.custom(context_lens=(), kv_dtype="fp8", **cfg)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    got = bf16_f64(host_bits(case.prefill()))
+    ma, mr = assert_close(got, _oracle_prefill(w, kc, vc), *TOL_FP8, what="fp8 prefill")
+    print(f"max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_prefill_fp8_matches_fp8_decode():
+    """A one-row prefill over an fp8 cache equals the fp8 decode of the same rows to
+    bf16 rounding (both widen the same bytes exactly and fold the same scales)."""
+    w = W.custom(seed=325, Hq=16, Hkv=4, D=128, bs=64, context_lens=(1, 100, 700), kv_dtype="fp8")
+    case = GpuCase(w)
+    dec = bf16_f64(host_bits(case.decode()))
+    import paged_kv_cache_store_amd as pa
+    S = w.num_seqs
+    cu_k = np.concatenate([[0], np.cumsum(w.context_lens)])
+    pre = pa.prefill_varlen(case.q, case.k_cache, case.v_cache, dev_i32(np.arange(S + 1)), dev_i32(cu_k),
+                            case.block_tables, float(w.scale), 1, int(w.context_lens.max()),
+                            k_scale=case.k_scale, v_scale=case.v_scale)
+    np.testing.assert_allclose(bf16_f64(host_bits(pre)), dec, rtol=2 ** -7, atol=2e-3)
+
+
 def test_mixed_chunked_prefill_workload():
     """Full mixed step: store of 4344 tokens, prefill of the 8 chunks (all rows checked),
     decode of the 248 sequences (all checked)."""
@@ -54,6 +91,22 @@ def test_mixed_chunked_prefill_workload():
     ref = oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.block_size)
     ma, mr = assert_close(dec, ref, *TOL, what="mixed decode")
     print(f"[mixed decode] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_mixed_chunked_prefill_fp8_workload():
+    """The same mixed step over an fp8 cache: all prefill rows, 32 sampled decode rows."""
+    w = W.make(6)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    pre = bf16_f64(host_bits(case.prefill()))
+    ma, mr = assert_close(pre, _oracle_prefill(w, kc, vc), *TOL_FP8, what="fp8 mixed prefill")
+    print(f"[fp8 mixed prefill] max_abs={ma:.3e} max_rel={mr:.3e}")
+    seqs = np.sort(np.random.default_rng(6).choice(w.num_seqs, size=32, replace=False))
+    dec = bf16_f64(host_bits(case.decode()))
+    ref = oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.block_size,
+                                  w.k_scale, w.v_scale, seqs=seqs)
+    ma, mr = assert_close(dec[seqs], ref[seqs], *TOL_FP8, what="fp8 mixed decode")
+    print(f"[fp8 mixed decode, 32 sampled] max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
 def test_chunk_equals_tail_of_full_prefill_bit_identical():

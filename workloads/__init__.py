@@ -319,8 +319,16 @@ def fp8_long_decode(seed: int = 1005, num_seqs: int = 64, lo: int = 8192, hi: in
                   seqs=_lengths(seed, num_seqs, lo, hi), kv_dtype="fp8", partition_size=1024)
 
 
+def mixed_chunked_prefill_fp8(seed: int = 1006) -> Workload:
+    """The mixed chunked-prefill + decode step over an FP8-e4m3 KV cache (per-KV-head
+    scales); same shapes and length recipe as the bf16 one."""
+    return _build(6, "mixed chunked prefill + decode, fp8 KV", seed=seed, Hq=32, Hkv=8, D=128, bs=256,
+                  seqs=_lengths(seed, 248, 100, 2048), prefill=[(256 * i, 512) for i in range(8)],
+                  kv_dtype="fp8")
+
+
 WORKLOADS = {1: tiny_decode, 2: qwen3_06b_decode, 3: qwen3_8b_decode,
-             4: mixed_chunked_prefill, 5: fp8_long_decode}
+             4: mixed_chunked_prefill, 5: fp8_long_decode, 6: mixed_chunked_prefill_fp8}
 
 
 def make(number: int, **kw) -> Workload:
