@@ -12,6 +12,7 @@ Modules
                   a block table, in the library's physical layout.
 * ``attention`` — decode and causal varlen prefill attention, written as the
                   dense definition on the de-paged keys/values.
+* ``norm``      — residual add + RMSNorm, and float64 -> bf16 rounding.
 
 What pins each function (none is pinned only against itself):
 * fp8.encode/decode — exhaustive comparison with torch's float8_e4m3fn cast
@@ -26,5 +27,11 @@ What pins each function (none is pinned only against itself):
   and invariants (physical-block permutation, shared prefix vs private
   copies, GQA vs replicated MHA, chunked prefill vs full causal prefill,
   decode vs prefill with one query row).
+* norm.f64_to_bf16_bits — hand cases (ties to even, a case where rounding via
+  float32 would differ, overflow, subnormals, signed zero, NaN) and torch's
+  float32 -> bfloat16 cast on float32 inputs.
+* norm.add_rmsnorm — torch's rms_norm in float64, torch's bfloat16 addition
+  for the residual sum, and closed forms (constant rows, one-hot rows, scale
+  invariance).
 """
-from . import fp8, cache, attention  # noqa: F401
+from . import fp8, cache, attention, norm  # noqa: F401

@@ -318,4 +318,100 @@ def pin_gqa_equals_replicated_mha():
     assert np.array_equal(gqa, mha)
 
 
+# ---------------------------------------------------------------- add + RMSNorm
+def _bits(a):
+    return np.asarray(a, dtype=np.uint16)
+
+
+def pin_bf16_round_hand_cases():
+    """float64 -> bf16 rounding: ties to even, one rounding step, range ends."""
+    cases = [(1.0, 0x3F80), (3.140625, 0x4049), (1 + 2 ** -8, 0x3F80), (1 + 3 * 2 ** -8, 0x3F82),
+             (1 + 2 ** -8 + 2 ** -30, 0x3F81),      # via float32 this would tie and go to 0x3F80
+             (-(1 + 2 ** -8 + 2 ** -30), 0xBF81), (0.0, 0x0000), (-0.0, 0x8000),
+             ((2 - 2 ** -7) * 2.0 ** 127, 0x7F7F), ((2 - 2 ** -8) * 2.0 ** 127, 0x7F80),
+             ((2 - 2 ** -8 - 2 ** -20) * 2.0 ** 127, 0x7F7F), (2.0 ** -126, 0x0080),
+             (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000), (3 * 2.0 ** -134, 0x0002),
+             (np.inf, 0x7F80), (-np.inf, 0xFF80), (1e300, 0x7F80)]
+    v = np.array([c[0] for c in cases])
+    got = oracle.norm.f64_to_bf16_bits(v)
+    want = _bits([c[1] for c in cases])
+    assert np.array_equal(got, want), [(c[0], hex(g)) for c, g, e in zip(cases, got, want) if g != e]
+    assert (oracle.norm.f64_to_bf16_bits(np.array([np.nan])) & 0x7FC0) == 0x7FC0
+
+
+def pin_bf16_round_vs_torch():
+    """On float32 inputs (where one rounding from float64 equals one from float32)
+    the rounding equals torch's float32 -> bfloat16 cast, exact ties included."""
+    rng = np.random.default_rng(81)
+    u = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, size=20000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    u = np.concatenate([u, ties, ties ^ 1])
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.norm.f64_to_bf16_bits(f.astype(np.float64)), want)
+
+
+def pin_rmsnorm_vs_torch():
+    """y against torch's rms_norm (float64) of x + r, with and without a residual."""
+    for seed, T, H, eps, res in ((84, 7, 64, 1e-6, True), (85, 3, 1000, 1e-5, True),
+                                 (86, 5, 128, 0.5, False), (87, 2, 4096, 1e-6, True),
+                                 (88, 4, 96, 3.0, True)):
+        x, r, w = W.norm_inputs(seed, T, H)
+        y, hb = oracle.norm.add_rmsnorm(x, w, eps, r if res else None)
+        h = torch.from_numpy(bf16_f64(x))
+        if res:
+            h = h + torch.from_numpy(bf16_f64(r))
+        ref = torch.nn.functional.rms_norm(h, (H,), torch.from_numpy(bf16_f64(w)), eps).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+        assert (hb is None) == (not res)
+
+
+def pin_residual_sum_vs_torch_bf16_add():
+    """The new residual equals torch's bfloat16 addition (float32 sum rounded to
+    nearest even, which is exact rounding for two bf16 operands) — over rows
+    whose residual is scaled by 2^-24 .. 2^24, r = -x rows and r = 0 rows."""
+    T, H = 52, 256
+    x, r, w = W.norm_inputs(89, T, H)
+    k = np.arange(T) - 24
+    r = W.f32_to_bf16_bits(W.bf16_bits_to_f32(r) * np.exp2(k).astype(np.float32)[:, None])
+    r[-2] = x[-2] ^ np.uint16(0x8000)          # h = 0
+    r[-1] = 0
+    _, hb = oracle.norm.add_rmsnorm(x, w, 1e-6, r)
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    tr = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16)
+    want = (tx + tr).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(hb, want)
+    assert np.array_equal(hb[-1], x[-1]) and not hb[-2].any()
+
+
+def pin_rmsnorm_closed_forms():
+    """Constant rows give sign(c) (eps 0, w 1); a one-hot row gives ±sqrt(H) at its
+    entry; scaling x by a power of two changes nothing (eps 0); mean((y/w)^2) is
+    ms / (ms + eps)."""
+    H = 96
+    ones = W.f32_to_bf16_bits(np.ones(H, np.float32))
+    c = np.array([-3.0, 0.5, 2.0 ** -10, 1024.0])
+    x = W.f32_to_bf16_bits(np.repeat(c[:, None], H, 1).astype(np.float32))
+    y, _ = oracle.norm.add_rmsnorm(x, ones, 0.0)
+    assert np.array_equal(y, np.repeat(np.sign(c)[:, None], H, 1))
+    oh = np.zeros((2, H), np.float32)
+    oh[0, 5], oh[1, 77] = 3.0, -0.25
+    y, _ = oracle.norm.add_rmsnorm(W.f32_to_bf16_bits(oh), ones, 0.0)
+    want = np.zeros((2, H))
+    want[0, 5], want[1, 77] = np.sqrt(H), -np.sqrt(H)
+    np.testing.assert_allclose(y, want, rtol=1e-15, atol=0)
+    xb, rb, wb = W.norm_inputs(90, 3, H)
+    y1, _ = oracle.norm.add_rmsnorm(xb, wb, 0.0, rb)
+    s = np.float32(2.0 ** 9)
+    y2, _ = oracle.norm.add_rmsnorm(W.f32_to_bf16_bits(W.bf16_bits_to_f32(xb) * s), wb, 0.0,
+                                    W.f32_to_bf16_bits(W.bf16_bits_to_f32(rb) * s))
+    assert np.array_equal(y1, y2)
+    eps = 7.0
+    y3, _ = oracle.norm.add_rmsnorm(xb, wb, eps, rb)
+    h = bf16_f64(xb) + bf16_f64(rb)
+    ms = (h ** 2).sum(1) / H
+    np.testing.assert_allclose(((y3 / bf16_f64(wb)) ** 2).sum(1) / H, ms / (ms + eps), rtol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -23,6 +23,8 @@ ATTN_PINS = [pins.pin_decode_vs_sdpa, pins.pin_prefill_vs_sdpa, pins.pin_chunk_i
 FP8_PINS = [pins.pin_fp8_code_table, pins.pin_fp8_encode_vs_torch, pins.pin_fp8_hand_cases,
             pins.pin_fp8_roundtrip]
 CACHE_PINS = [pins.pin_store_roundtrip, pins.pin_layout_offsets, pins.pin_store_skip_and_sentinel]
+NORM_PINS = [pins.pin_bf16_round_hand_cases, pins.pin_bf16_round_vs_torch, pins.pin_rmsnorm_vs_torch,
+             pins.pin_residual_sum_vs_torch_bf16_add, pins.pin_rmsnorm_closed_forms]
 
 
 def _interleaved_heads(h, group, num_kv_heads):
@@ -73,6 +75,29 @@ def _depage_swapped_v(k_cache, v_cache, table_row, length, block_size, k_scale=N
     return K, V
 
 
+def _residual_dropped(x, r):
+    return x
+
+
+def _mean_over_h_minus_1(h):
+    return np.sum(h * h, axis=-1, keepdims=True) / (h.shape[-1] - 1)
+
+
+def _bf16_via_float32(v):
+    import workloads as W
+    return W.f32_to_bf16_bits(np.asarray(v, dtype=np.float64).astype(np.float32))
+
+
+def _bf16_ties_away(v):
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    step = np.exp2(np.maximum(ex - 1, -126) - 7.0)
+    q = np.floor(a / step + 0.5) * step
+    q = np.where(np.signbit(v), -q, q)
+    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 MUTATIONS = [
     ("attention._kv_head", _interleaved_heads, ATTN_PINS),
     ("attention._causal_mask", _top_left_mask, ATTN_PINS),
@@ -81,6 +106,10 @@ MUTATIONS = [
     ("fp8._tie_break", _ties_up, FP8_PINS),
     ("fp8.decode", _decode_off_by_one_exponent, FP8_PINS),
     ("cache.depage_raw", _depage_swapped_v, CACHE_PINS),
+    ("norm._residual_sum", _residual_dropped, NORM_PINS),
+    ("norm._mean_square", _mean_over_h_minus_1, NORM_PINS),
+    ("norm.f64_to_bf16_bits", _bf16_via_float32, NORM_PINS),
+    ("norm.f64_to_bf16_bits", _bf16_ties_away, NORM_PINS),
 ]
 
 

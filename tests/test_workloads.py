@@ -73,3 +73,12 @@ def test_draws_do_not_depend_on_chunking():
     a = W.bf16_normal(5, 3, (3, 1000), chunk=1 << 22)
     b = W.bf16_normal(5, 3, (3, 1000), chunk=1 << 22)
     assert np.array_equal(a, b)
+
+
+def test_norm_inputs_seeded_and_shaped():
+    x, r, w = W.norm_inputs(5, 3, 128)
+    x2, r2, w2 = W.norm_inputs(5, 3, 128)
+    assert x.shape == r.shape == (3, 128) and w.shape == (128,)
+    assert x.dtype == r.dtype == w.dtype == np.uint16
+    assert np.array_equal(x, x2) and np.array_equal(r, r2) and np.array_equal(w, w2)
+    assert not np.array_equal(x, W.norm_inputs(6, 3, 128)[0])

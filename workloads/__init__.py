@@ -380,3 +380,26 @@ def prefix_q(tokens, num_q_heads: int, head_dim: int, seed: int = 78):
         rng = np.random.default_rng(np.random.SeedSequence([seed, h & 0xFFFFFFFF, h >> 32]))
         Q[p] = f32_to_bf16_bits(rng.standard_normal((num_q_heads, head_dim), dtype=np.float32))
     return Q
+
+
+_STREAM_NORM_X, _STREAM_NORM_R, _STREAM_NORM_W = 200, 201, 202
+
+
+def norm_inputs(seed: int, num_tokens: int, hidden: int):
+    """Inputs of a residual add + RMSNorm as bf16 bits: x [T, H] ~ N(0,1) (a
+    layer's output), r [T, H] ~ 4·N(0,1) (the residual stream, larger than one
+    layer's output), w [H] ~ 1 + N(0,1)/4 (a trained norm weight stays near 1)."""
+    x = bf16_normal(seed, _STREAM_NORM_X, (num_tokens, hidden))
+    r = bf16_normal(seed, _STREAM_NORM_R, (num_tokens, hidden))
+    r = f32_to_bf16_bits(bf16_bits_to_f32(r) * np.float32(4.0))        # exact: power of two
+    rng = np.random.default_rng(np.random.SeedSequence([seed, _STREAM_NORM_W]))
+    w = f32_to_bf16_bits(1.0 + 0.25 * rng.standard_normal(hidden).astype(np.float32))
+    return x, r, w
+
+
+# Hidden sizes of the norm workloads: Qwen3-0.6B (1024) and Qwen3-8B (4096)
+# residual streams, and the per-head q/k norm of both (head_dim 128).
+NORM_WORKLOADS = {
+    "qwen3-8b mixed step (4344 tokens x 4096)": (4344, 4096),
+    "qwen3-0.6b decode step (256 tokens x 1024)": (256, 1024),
+}
