@@ -185,11 +185,7 @@ def run_steps(st, steps, warmup, graph=True):
     torch = st.torch
     calls = [("store", st.store)]
     if st.w.has_prefill:
-        try:
-            st.prefill()
-            calls.append(("prefill", st.prefill))
-        except st.pa.PaError as e:          # prefill kernel not in this build
-            log(f"[bench] prefill skipped: {e}")
+        calls.append(("prefill", st.prefill))
     calls.append(("decode", st.decode))
     for _ in range(warmup):
         for _, f in calls:
@@ -227,6 +223,44 @@ def run_steps(st, steps, warmup, graph=True):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) * 1e3 / steps, ms, ms_eager
+
+
+def norm_bench(torch, T, H, steps, warmup):
+    """Time pa_add_rmsnorm (with residual) on [T, H] bf16 rows: a HIP graph of 20
+    launches replayed `steps` times between HIP events on the launch stream.
+    Algorithmic bytes: x and r read, y and the new residual
+    written (4·T·H·2) plus the weight once (H·2)."""
+    import paged_kv_cache_store_amd as pa
+    import workloads as W
+    x, r, w = W.norm_inputs(7, T, H)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    xd, rd, wd = dev(x), dev(r), dev(w)
+    out, hres = torch.empty_like(xd), torch.empty_like(xd)
+    reps = 20          # launches per graph: the small shapes would time the host otherwise
+
+    def launches():
+        for _ in range(reps):
+            pa.add_rmsnorm(xd, wd, 1e-6, residual=rd, out=out, residual_out=hres)
+
+    g = pa.capture_step(launches)
+    for _ in range(warmup):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (steps * reps)
+    nbytes = 4 * T * H * 2 + H * 2
+    return {"TBps": round(nbytes / (ms * 1e-3) / 1e12, 4), "ms": round(ms, 5), "bytes": nbytes,
+            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS, 4)}
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -375,6 +409,9 @@ def main():
                             "prefill_frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                             "prefill_flops": e["prefill_flops"]})
             extra[e["w"].name] = ent
+        for name, (T, H) in W.NORM_WORKLOADS.items():
+            log(f"[bench] add_rmsnorm {name}")
+            extra["add_rmsnorm: " + name] = norm_bench(torch, T, H, 10, 2)
         line["other_workloads"] = extra
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")

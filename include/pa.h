@@ -163,6 +163,30 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                             int32_t max_seqlen_k, float scale, void* out,
                             const pa_cache_desc* cache, hipStream_t stream);
 
+/* pa_add_rmsnorm — residual add fused with RMSNorm in one pass over each row, so
+ * the sum is normalised without a round trip through memory ("nano-vllm-lite…",
+ * 核心技术改进 §1):
+ *     h = x + residual        (residual NULL: h = x, plain RMSNorm)
+ *     out = h * weight / sqrt(mean(h^2) + eps),  mean over the hidden dimension
+ *   x             device bf16 [num_tokens][hidden], contiguous
+ *   residual      device bf16 [num_tokens][hidden], or NULL
+ *   weight        device bf16 [hidden]
+ *   out           device bf16 [num_tokens][hidden]
+ *   residual_out  device bf16 [num_tokens][hidden]: receives h rounded to nearest
+ *                 even bf16 (the same bits as rounding the exact sum); required
+ *                 when residual is given, ignored otherwise
+ *   hidden        a multiple of 8, at most 16384 (else PA_ERR_UNSUPPORTED)
+ *   eps           finite and > 0 (else PA_ERR_SHAPE)
+ * Float32 arithmetic: h and the sum of squares in float32, out rounded once to
+ * nearest-even bf16. In place is allowed: out and residual_out may each be the
+ * same pointer as x or residual (every element is read before it is written);
+ * out == residual_out is PA_ERR_SHAPE and any other overlap is undefined. All
+ * pointers must be 16-byte aligned (else PA_ERR_UNSUPPORTED). num_tokens == 0 is
+ * a no-op. */
+pa_status pa_add_rmsnorm(const void* x, const void* residual, const void* weight,
+                         int32_t num_tokens, int32_t hidden, float eps, void* out,
+                         void* residual_out, hipStream_t stream);
+
 /* Static text for a status code; never NULL. */
 const char* pa_status_string(pa_status s);
 

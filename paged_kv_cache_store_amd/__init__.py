@@ -56,7 +56,8 @@ def _load():
     lib.pa_decode_partition_size.restype = I32
     lib.pa_decode.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
     lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
-    for name in ("pa_store_kv", "pa_decode", "pa_prefill_varlen"):
+    lib.pa_add_rmsnorm.argtypes = [P, P, P, I32, I32, F, P, P, P]
+    for name in ("pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_add_rmsnorm"):
         getattr(lib, name).restype = ctypes.c_int
     I64, PI32, PI64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -241,6 +242,37 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
     if st != 0:
         raise PaError(st, "pa_prefill_varlen")
     return out
+
+
+def add_rmsnorm(x, weight, eps, residual=None, out=None, residual_out=None, stream=None):
+    """Residual add fused with RMSNorm over the last dimension (see pa.h).
+    x, residual, out, residual_out: bf16 [T, H] on one device; weight bf16 [H].
+    Returns out, or (out, residual_out) when a residual is given. Passing
+    out=x and residual_out=residual works in place."""
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    T, H = x.shape
+    _check(weight, "weight", torch.bfloat16, 1, dev)
+    if weight.shape[0] != H:
+        raise ValueError(f"weight has {weight.shape[0]} entries for hidden size {H}")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", torch.bfloat16, 2, dev)
+    if tuple(out.shape) != (T, H):
+        raise ValueError("out must have the shape of x")
+    if residual is not None:
+        _check(residual, "residual", torch.bfloat16, 2, dev)
+        if residual_out is None:
+            residual_out = torch.empty_like(x)
+        _check(residual_out, "residual_out", torch.bfloat16, 2, dev)
+        if tuple(residual.shape) != (T, H) or tuple(residual_out.shape) != (T, H):
+            raise ValueError("residual and residual_out must have the shape of x")
+    st = library().pa_add_rmsnorm(_ptr(x), _ptr(residual) if residual is not None else None, _ptr(weight),
+                                  T, H, float(eps), _ptr(out),
+                                  _ptr(residual_out) if residual is not None else None, _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_add_rmsnorm")
+    return out if residual is None else (out, residual_out)
 
 
 def capture_step(fn, warmup=1):

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "rmsnorm.hip", "block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = [

@@ -177,4 +177,21 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                                        cache->k_scale, cache->v_scale, stream));
 }
 
+pa_status pa_add_rmsnorm(const void* x, const void* residual, const void* weight, int32_t num_tokens,
+                         int32_t hidden, float eps, void* out, void* residual_out, hipStream_t stream) {
+  if (num_tokens < 0 || hidden <= 0) return PA_ERR_SHAPE;
+  if (hidden % 8 != 0 || hidden > 16384) return PA_ERR_UNSUPPORTED;
+  if (!(eps > 0.f) || eps == INFINITY) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!x || !weight || !out || (residual && !residual_out)) return PA_ERR_NULL;
+  if (residual && residual_out == out) return PA_ERR_SHAPE;
+  const void* ptrs[5] = {x, residual, weight, out, residual ? residual_out : nullptr};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  return hip_status(pa::launch_add_rmsnorm(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(residual),
+      static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(out),
+      residual ? static_cast<uint16_t*>(residual_out) : nullptr, num_tokens, hidden, eps, stream));
+}
+
 }  // extern "C"

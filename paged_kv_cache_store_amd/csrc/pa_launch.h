@@ -40,4 +40,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
                           const PoolDims& pool, const float* k_scale, const float* v_scale,
                           hipStream_t stream);
 
+hipError_t launch_add_rmsnorm(const uint16_t* x, const uint16_t* r, const uint16_t* w, uint16_t* out,
+                              uint16_t* r_out, int num_tokens, int hidden, float eps, hipStream_t stream);
+
 }  // namespace pa

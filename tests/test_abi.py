@@ -104,3 +104,24 @@ def test_prefill_validation(lib):
     assert prefill(lib, desc(), S=0, q=None) == OK
     for bad in (0.0, -0.5, float("inf"), float("nan")):
         assert prefill(lib, desc(), scale=bad) == SHAPE
+
+
+def norm(lib, x=FAKE, r=FAKE, w=FAKE, T=4, H=64, eps=1e-6, out=ctypes.c_void_p(0x2000),
+         rout=ctypes.c_void_p(0x3000)):
+    return lib.pa_add_rmsnorm(x, r, w, T, H, eps, out, rout, None)
+
+
+def test_add_rmsnorm_validation(lib):
+    assert norm(lib, T=-1) == SHAPE
+    assert norm(lib, H=0) == SHAPE
+    assert norm(lib, H=12) == UNSUP                          # not a multiple of 8
+    assert norm(lib, H=16392) == UNSUP                       # above 16384
+    for bad in (0.0, -1e-6, float("inf"), float("nan")):
+        assert norm(lib, eps=bad) == SHAPE
+    assert norm(lib, T=0, x=None, r=None, w=None, out=None, rout=None) == OK
+    assert norm(lib, x=None) == NULL
+    assert norm(lib, w=None) == NULL
+    assert norm(lib, rout=None) == NULL                      # residual given, no residual_out
+    assert norm(lib, rout=ctypes.c_void_p(0x2000)) == SHAPE  # residual_out == out
+    assert norm(lib, x=ctypes.c_void_p(0x1002)) == UNSUP     # not 16-byte aligned
+    assert norm(lib, rout=ctypes.c_void_p(0x3008)) == UNSUP

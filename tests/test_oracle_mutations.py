@@ -85,7 +85,8 @@ def _mean_over_h_minus_1(h):
 
 def _bf16_via_float32(v):
     import workloads as W
-    return W.f32_to_bf16_bits(np.asarray(v, dtype=np.float64).astype(np.float32))
+    with np.errstate(over="ignore"):
+        return W.f32_to_bf16_bits(np.asarray(v, dtype=np.float64).astype(np.float32))
 
 
 def _bf16_ties_away(v):
@@ -95,7 +96,8 @@ def _bf16_ties_away(v):
     step = np.exp2(np.maximum(ex - 1, -126) - 7.0)
     q = np.floor(a / step + 0.5) * step
     q = np.where(np.signbit(v), -q, q)
-    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    with np.errstate(over="ignore"):
+        return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 MUTATIONS = [

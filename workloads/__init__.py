@@ -397,8 +397,9 @@ def norm_inputs(seed: int, num_tokens: int, hidden: int):
     return x, r, w
 
 
-# Hidden sizes of the norm workloads: Qwen3-0.6B (1024) and Qwen3-8B (4096)
-# residual streams, and the per-head q/k norm of both (head_dim 128).
+# Shapes of the norm workloads: the residual streams of Qwen3-8B (hidden 4096)
+# over the tokens of the mixed chunked-prefill step, and of Qwen3-0.6B (1024)
+# over the tokens of its decode step.
 NORM_WORKLOADS = {
     "qwen3-8b mixed step (4344 tokens x 4096)": (4344, 4096),
     "qwen3-0.6b decode step (256 tokens x 1024)": (256, 1024),
