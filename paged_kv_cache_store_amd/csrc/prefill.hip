@@ -86,7 +86,7 @@ static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
 // (query row, head) columns, i.e. 128 * kNB / G query rows of each of the G heads.
-template <int kD, int kG, int kNB, bool kFp8>
+template <int kD, int kG, int kNB, bool kFp8, bool kBig>
 __global__ __launch_bounds__(kPrefillThreads)
 #if PA_PREFILL_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
@@ -102,7 +102,7 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kVLoads = (kBN / kX) * kD / kPrefillThreads;
 
   __shared__ uint4 k_s[2][kKC][kBN];
-  __shared__ uint4 v_s[2][kBN / 16][kD][2];
+  __shared__ uint4 v_s[2][kBN / 16][2][kD];
 
   const int Hkv = a.num_kv_heads;
   const int bid = blockIdx.x;
@@ -166,9 +166,10 @@ void prefill_kernel(const PrefillArgs a) {
   // K: thread t always loads key (t % 64) of the tile, chunks t/64 + 4u: one
   // block-table lookup per tile. V: thread t loads head-dim index t % D of the
   // tile's 8-key chunks. Block sizes are powers of two (shift/mask).
-  // LDS V layout per 16-key step s: [d][h][16 bytes] holding keys
+  // LDS V layout per 16-key step s: [h][d][16 bytes] holding keys
   // {4h..4h+3} and {8+4h..8+4h+3} of the step, the order in which the P^T
-  // accumulator hands keys to lane half h, so an A fragment is one 16-byte read.
+  // accumulator hands keys to lane half h, so an A fragment is one 16-byte read
+  // and the 32 lanes of a half read 512 contiguous bytes (no bank conflict).
   const int bshift = a.block_shift;
   const int bmask = bs - 1;
   const int k_key = tid % kBN;            // K: this thread's key within the tile
@@ -180,19 +181,44 @@ void prefill_kernel(const PrefillArgs a) {
   u32x4_t kreg[kKLoads], vreg[kVLoads];
   // block ids are fetched one tile before the loads that use them, so the
   // K/V loads never wait on a dependent block-table read
-  struct TileIds { int k; int v[kVLoads]; };
+  // With blocks of at least one tile (kBig) a tile lies inside one block: its id
+  // is one scalar load, the tile's base address is scalar and every lane's
+  // offset is fixed for the whole loop. Keys past Lk in the last tile then read
+  // slots of that block past the context: in bounds, their scores masked, their
+  // V values zeroed before use.
+  struct TileIds { int k; int v[kBig ? 1 : kVLoads]; };
+  uint32_t koff[kKLoads], voff[kVLoads];   // kBig: per-lane offsets (16-byte units)
+#pragma unroll
+  for (int u = 0; u < kKLoads; ++u) koff[u] = uint32_t((k_c0 + u * (kPrefillThreads / kBN)) << bshift) + k_key;
+#pragma unroll
+  for (int u = 0; u < kVLoads; ++u) voff[u] = uint32_t((v_j0 + u * (kPrefillThreads / kD)) * kD + v_d);
   auto fetch_ids = [&](int kt, TileIds& ids) {
     const int key0 = kt * kBN;
+    if constexpr (kBig) {
+      ids.k = bt[key0 >> bshift];
+      return;
+    }
     const int key = key0 + k_key;
     ids.k = bt[(key < Lk ? key : Lk - 1) >> bshift];
 #pragma unroll
-    for (int u = 0; u < kVLoads; ++u) {
+    for (int u = 0; u < (kBig ? 1 : kVLoads); ++u) {
       const int vkey = key0 + (v_j0 + u * (kPrefillThreads / kD)) * kX;
       ids.v[u] = bt[(vkey < Lk ? vkey : Lk - 1) >> bshift];
     }
   };
   auto load_tile = [&](int kt, const TileIds& ids) {
     const int key0 = kt * kBN;
+    if constexpr (kBig) {
+      const long long base = (long long)ids.k * blk16 + (key0 & bmask);
+      const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(kpool + base);
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u) kreg[u] = kb[koff[u]];
+      const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(vpool + (long long)ids.k * blk16 +
+                                                           (long long)((key0 & bmask) / kX) * kD);
+#pragma unroll
+      for (int u = 0; u < kVLoads; ++u) vreg[u] = vb[voff[u]];
+      return;
+    }
     {
       const int key = key0 + k_key;
       const int kc = key < Lk ? key : Lk - 1;
@@ -207,7 +233,7 @@ void prefill_kernel(const PrefillArgs a) {
       const int j = v_j0 + u * (kPrefillThreads / kD);   // x-key chunk of the tile
       const int key = key0 + j * kX;
       const int kc = key < Lk ? key : ((Lk - 1) & ~(kX - 1));
-      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[u] * blk16 + (long long)((kc & bmask) / kX) * kD + v_d];
+      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[kBig ? 0 : u] * blk16 + (long long)((kc & bmask) / kX) * kD + v_d];
     }
   };
   // V values past Lk are zeroed here, where the loads have landed anyway (their
@@ -233,9 +259,8 @@ void prefill_kernel(const PrefillArgs a) {
         const int j = v_j0 + u * (kPrefillThreads / kD);
         const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
         // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
-        uint2* dst = reinterpret_cast<uint2*>(&v_s[buf][step][v_d][0]);
-        dst[0 * 2 + second] = make_uint2(vreg[u][0], vreg[u][1]);
-        dst[1 * 2 + second] = make_uint2(vreg[u][2], vreg[u][3]);
+        reinterpret_cast<uint2*>(&v_s[buf][step][0][v_d])[second] = make_uint2(vreg[u][0], vreg[u][1]);
+        reinterpret_cast<uint2*>(&v_s[buf][step][1][v_d])[second] = make_uint2(vreg[u][2], vreg[u][3]);
       }
     } else {
       // fp8 pool: a 16-byte chunk holds 16 values; converted exactly to bf16 here
@@ -272,8 +297,8 @@ void prefill_kernel(const PrefillArgs a) {
           w[2 * i] = fp8x2_to_bf16x2<false>(vreg[u][i]);
           w[2 * i + 1] = fp8x2_to_bf16x2<true>(vreg[u][i]);
         }
-        v_s[buf][step][v_d][0] = make_uint4(w[0], w[1], w[4], w[5]);
-        v_s[buf][step][v_d][1] = make_uint4(w[2], w[3], w[6], w[7]);
+        v_s[buf][step][0][v_d] = make_uint4(w[0], w[1], w[4], w[5]);
+        v_s[buf][step][1][v_d] = make_uint4(w[2], w[3], w[6], w[7]);
       }
     }
   };
@@ -396,7 +421,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const int d = db * 32 + l32;
-          const bf16x8_t af = as_bf16x8(v_s[buf][t][d][half]);
+          const bf16x8_t af = as_bf16x8(v_s[buf][t][half][d]);
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb)
             o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
@@ -434,15 +459,21 @@ void prefill_kernel(const PrefillArgs a) {
 
 constexpr int kNBLaunch = PA_PREFILL_NB;
 
-template <int kD, bool kFp8>
-static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
+template <int kD, bool kFp8, bool kBig>
+static bool launch_prefill_gb(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   switch (G) {
-    case 1: prefill_kernel<kD, 1, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 2: prefill_kernel<kD, 2, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 4: prefill_kernel<kD, 4, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 8: prefill_kernel<kD, 8, kNBLaunch, kFp8><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 1: prefill_kernel<kD, 1, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 2: prefill_kernel<kD, 2, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 4: prefill_kernel<kD, 4, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 8: prefill_kernel<kD, 8, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
     default: return false;
   }
+}
+
+template <int kD, bool kFp8>
+static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
+  return a.block_size >= kBN ? launch_prefill_gb<kD, kFp8, true>(G, a, grid, stream)
+                             : launch_prefill_gb<kD, kFp8, false>(G, a, grid, stream);
 }
 
 hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
