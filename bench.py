@@ -13,8 +13,9 @@ them as separate calls; both figures are in the line).
 Inputs are resident in HBM before the timed region. `value` is the step's
 algorithmic bytes (unique KV bytes read by decode and prefill, q/out, tables,
 plus the store's reads and writes) divided by the wall time per step. The
-`roofline` object is the dominant call (pa_decode) timed with HIP events on
-the stream it runs on. `cpu_baseline` times the CPU oracle (numpy float64) on
+`roofline` object is the dominant call (pa_decode) timed on its own: a HIP
+graph of 10 back-to-back launches replayed between HIP events on the stream it
+runs on (per-call figures of the other calls are taken the same way). `cpu_baseline` times the CPU oracle (numpy float64) on
 a bounded sample of the same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 2]
@@ -105,7 +106,7 @@ def decode_traffic():
     fields = dict(line.split(": ", 1) for line in text.splitlines()
                   if line.startswith(("traffic_bytes_per_launch: ", "decode_source_sha256: ")))
     h = hashlib.sha256()
-    for f in ("decode.hip", "pa_device.h", "pa_launch.h"):
+    for f in ("decode.hip", "pa_device.h"):       # the sources that define the decode kernel
         with open(os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if fields.get("decode_source_sha256", "").strip() != h.hexdigest():
@@ -177,11 +178,30 @@ class Setup:
                                v_scale=self.vs)
 
 
+def time_launches(pa, torch, fn, reps, iters):
+    """GPU time of one call of fn: a HIP graph of `reps` back-to-back calls,
+    replayed `iters` times between two HIP events on the launch stream (so no
+    host-side gap between launches is counted). Returns ms per call."""
+    g = pa.capture_step(lambda: [fn() for _ in range(reps)])
+    g.replay()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(iters):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (reps * iters)
+
+
 def run_steps(st, steps, warmup, graph=True):
-    """Warm up; time `steps` eager steps with HIP events around each call (on the
-    stream the library launches on); then, with graph=True, capture one step as a
-    HIP graph and time `steps` replays between two synchronisations.
-    Returns (ms per step, per-call ms, ms per eager step)."""
+    """Warm up; time `steps` eager steps (wall clock between synchronisations);
+    time each call on its own (time_launches); then, with graph=True, capture one
+    whole step as a HIP graph and time `steps` replays between two
+    synchronisations. Returns (ms per step, per-call ms, ms per eager step)."""
     torch = st.torch
     calls = [("store", st.store)]
     if st.w.has_prefill:
@@ -190,22 +210,15 @@ def run_steps(st, steps, warmup, graph=True):
     for _ in range(warmup):
         for _, f in calls:
             f()
-    stream = torch.cuda.current_stream()
-    ev = {name: [] for name, _ in calls}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        for name, f in calls:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+        for _, f in calls:
             f()
-            b.record(stream)
-            ev[name].append((a, b))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in pairs])) for name, pairs in ev.items()}
     ms_eager = (t1 - t0) * 1e3 / steps
+    ms = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4)) for name, f in calls}
     if not graph:
         return ms_eager, ms, ms_eager
 
