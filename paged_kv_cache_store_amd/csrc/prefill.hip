@@ -9,19 +9,21 @@
 // ("Nano-vLLM：轻量高效的大模型推理框架…", 三.3 模型层适配).
 //
 // Work decomposition (CDNA4, wave64, v_mfma_f32_32x32x16_bf16):
-// * one workgroup (4 waves) per (sequence, KV head, block of 256/G query rows);
-//   the G query heads of the KV head are packed into 256 rows, 64 per wave, so
-//   every K/V tile staged in LDS serves all G heads;
-// * K/V tiles of 64 keys are copied from the pool to LDS (double-buffered
-//   through registers): K in the pool's own layout [D/8][64][8], V as
-//   [4 steps][D][2 halves][8 keys];
+// * one workgroup (4 waves) per (sequence, KV head, block of 128/G query rows);
+//   the G query heads of the KV head are packed into 128 columns, 32 per wave,
+//   so every K/V tile staged in LDS serves all G heads;
+// * K/V tiles of 64 keys are copied from the pool to LDS, double-buffered, in
+//   the pool's own layouts: K [D/8][64 keys][8], V [8 chunks of 8 keys][D][8];
+//   bf16 tiles go straight from the pool into LDS (global_load_lds), fp8 tiles
+//   through registers, where they are widened to bf16;
 // * S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T from registers (loaded
 //   once), so each lane owns one query column and its softmax statistics;
 // * the row max needs one exchange with lane l^32; the weights P^T come out of
 //   the accumulator already in the B-operand layout of the next product;
 // * O^T += V^T P^T: A = V^T from LDS. The accumulator hands lane half h the keys
-//   {4h..4h+3, 8+4h..8+4h+3} of each 16-key step, so V is staged in LDS with its
-//   keys in that order and every A fragment is one 16-byte read.
+//   {4h..4h+3, 8+4h..8+4h+3} of each 16-key step; one v_permlane32_swap per
+//   dword pair regroups them to keys 8h..8h+7, one 8-key V chunk, so every A
+//   fragment is one 16-byte read.
 #include <math.h>
 
 #include "pa_device.h"
@@ -47,6 +49,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kBN = 64;           // keys per tile
+constexpr int kIdCache = 2048;    // block ids held in LDS at a time
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -87,6 +90,14 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// 16 bytes per lane from global memory into LDS at lds_row + 16 * lane
+// (global_load_lds: the data skips the registers; the wave's lanes land in
+// lane order). Plain void pointers: with the vector-struct pointer types the
+// host compilation pass drops the kernel's launch stub.
+__device__ __forceinline__ void load_row_to_lds(const void* src, void* lds_row) {
+  __builtin_amdgcn_global_load_lds(src, lds_row, 16, 0, 0);
+}
+
 static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
@@ -106,8 +117,19 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kKLoads = (kD / kX) * kBN / kPrefillThreads;   // 16-byte K loads per thread per tile
   constexpr int kVLoads = (kBN / kX) * kD / kPrefillThreads;
 
-  __shared__ uint4 k_s[2][kKC][kBN];
-  __shared__ uint4 v_s[2][kBN / 16][2][kD];
+  constexpr bool kDirect = !kFp8;        // bf16 tiles go from the pool straight into LDS
+  constexpr int kKW = kKC / kPrefillWaves;                   // direct: K chunk rows per wave
+  constexpr int kVW = (kBN / 8) * (kD / 64) / kPrefillWaves; // direct: 64-wide V rows per wave
+
+  // Two LDS buffers per tile, each in the pool's own order: K [16-byte chunk of
+  // head-dims][key] and V [8-key chunk][head-dim], 16 bytes per entry (bf16).
+  // Separate arrays (not one array indexed by buffer) let the compiler see that
+  // reads of one buffer never alias the copies in flight into the other, so it
+  // places no wait for those copies before the reads.
+  __shared__ uint4 k_a[kKC][kBN], k_b[kKC][kBN];
+  __shared__ uint4 v_a[kBN / 8][kD], v_b[kBN / 8][kD];
+  // a window of the sequence's block-table row: ids_s[i] = row[wbase + i]
+  __shared__ int ids_s[kIdCache];
 
   const int Hkv = a.num_kv_heads;
   const int bid = blockIdx.x;
@@ -167,144 +189,162 @@ void prefill_kernel(const PrefillArgs a) {
     for (int ks = 0; ks < kKS; ++ks) qf[nb][ks] = qp[ks * 2 + half];
   }
 
-  // ---- tile loader: pool -> registers -> LDS.
-  // K: thread t always loads key (t % 64) of the tile, chunks t/64 + 4u: one
-  // block-table lookup per tile. V: thread t loads head-dim index t % D of the
-  // tile's 8-key chunks. Block sizes are powers of two (shift/mask).
-  // LDS V layout per 16-key step s: [h][d][16 bytes] holding keys
-  // {4h..4h+3} and {8+4h..8+4h+3} of the step, the order in which the P^T
-  // accumulator hands keys to lane half h, so an A fragment is one 16-byte read
-  // and the 32 lanes of a half read 512 contiguous bytes (no bank conflict).
+  // ---- tile loader.
+  // Block ids come from a window of the block-table row kept in LDS (ids_s),
+  // loaded before the first tile and moved forward when a tile needs blocks
+  // past it. Block sizes are powers of two (shift/mask).
+  // bf16 (kDirect): each wave moves whole 1 KB rows of a tile from the pool
+  // into LDS with global_load_lds (16 bytes per lane, lane-major): K rows are
+  // (chunk c, 64 keys), V rows (8-key chunk j, 64 head-dims); no staging
+  // registers and no LDS writes by the waves. fp8: loads into registers,
+  // widening to bf16, LDS writes in the same layouts.
+  // With blocks of at least one tile (kBig) a tile lies inside one block: its
+  // base address is scalar and every lane's offset is the same for each tile.
+  // Keys past Lk in the last tile then read slots of that block past the
+  // context: in bounds, their scores masked, their V values zeroed before use.
+  // With smaller blocks keys past Lk read key Lk-1 (K) or the chunk holding it (V).
   const int bshift = a.block_shift;
   const int bmask = bs - 1;
-  const int k_key = tid % kBN;            // K: this thread's key within the tile
-  const int k_c0 = tid / kBN;             // K: first chunk (then + 4u)
-  const int v_d = tid % kD;               // V: head-dim index
-  const int v_j0 = tid / kD;              // V: first x-key chunk (then + kPrefillThreads/kD * u)
-  // staging registers use a native vector type: with HIP's union-based uint4 the
-  // array is not split into registers and the backend moves it into LDS
-  u32x4_t kreg[kKLoads], vreg[kVLoads];
-  // block ids are fetched one tile before the loads that use them, so the
-  // K/V loads never wait on a dependent block-table read
-  // With blocks of at least one tile (kBig) a tile lies inside one block: its id
-  // is one scalar load, the tile's base address is scalar and every lane's
-  // offset is fixed for the whole loop. Keys past Lk in the last tile then read
-  // slots of that block past the context: in bounds, their scores masked, their
-  // V values zeroed before use.
-  struct TileIds { int k; int v[kBig ? 1 : kVLoads]; };
-  uint32_t koff[kKLoads], voff[kVLoads];   // kBig: per-lane offsets (16-byte units)
-#pragma unroll
-  for (int u = 0; u < kKLoads; ++u) koff[u] = uint32_t((k_c0 + u * (kPrefillThreads / kBN)) << bshift) + k_key;
-#pragma unroll
-  for (int u = 0; u < kVLoads; ++u) voff[u] = uint32_t((v_j0 + u * (kPrefillThreads / kD)) * kD + v_d);
-  auto fetch_ids = [&](int kt, TileIds& ids) {
-    const int key0 = kt * kBN;
-    if constexpr (kBig) {
-      ids.k = bt[key0 >> bshift];
-      return;
-    }
-    const int key = key0 + k_key;
-    ids.k = bt[(key < Lk ? key : Lk - 1) >> bshift];
-#pragma unroll
-    for (int u = 0; u < (kBig ? 1 : kVLoads); ++u) {
-      const int vkey = key0 + (v_j0 + u * (kPrefillThreads / kD)) * kX;
-      ids.v[u] = bt[(vkey < Lk ? vkey : Lk - 1) >> bshift];
+  // blocks the workgroup's tiles touch
+  const int last_key = (ntiles * kBN < Lk ? ntiles * kBN : Lk) - 1;
+  const int nblk = last_key >= 0 ? (last_key >> bshift) + 1 : 0;
+  int wbase = 0;
+  auto load_ids = [&](int first) {   // every thread calls it; the caller synchronises
+    wbase = first;
+    for (int i = tid; i < kIdCache && first + i < nblk; i += kPrefillThreads) ids_s[i] = bt[first + i];
+  };
+  auto block_of = [&](int key) { return ids_s[(key >> bshift) - wbase]; };
+  // move the window so that it holds every block tile kt reads (uniform branch)
+  auto ensure_ids = [&](int kt) {
+    const int lastk = (kt * kBN + kBN < Lk ? kt * kBN + kBN : Lk) - 1;
+    if ((lastk >> bshift) - wbase >= kIdCache) {
+      __syncthreads();
+      load_ids((kt * kBN) >> bshift);
+      __syncthreads();
     }
   };
-  auto load_tile = [&](int kt, const TileIds& ids) {
+  const int k_key = tid % kBN;            // K: this lane's key within the tile
+  const int k_c0 = tid / kBN;             // staged K: first chunk (then + 4u)
+  const int v_d = tid % kD;               // staged V: head-dim index
+  const int v_j0 = tid / kD;              // staged V: first 16-key chunk
+  // staging registers use a native vector type: with HIP's union-based uint4 the
+  // array is not split into registers and the backend moves it into LDS
+  u32x4_t kreg[kDirect ? 1 : kKLoads], vreg[kDirect ? 1 : kVLoads];
+  // direct: the V row filled by load u of this wave: 8-key chunk j, head-dims 64*dh ..
+  auto vrow = [&](int u, int& j, int& dh) {
+    const int e = w * kVW + u;
+    j = e / (kD / 64);
+    dh = e % (kD / 64);
+  };
+  // direct: issue the pool -> LDS copies of tile kt into the buffers ks / vs
+  auto issue_tile = [&](int kt, uint4 (*ks)[kBN], uint4 (*vs)[kD]) {
+    const int key0 = kt * kBN;
+    const int kkey = key0 + k_key < Lk ? key0 + k_key : Lk - 1;
+    const int kblk = kBig ? __builtin_amdgcn_readfirstlane(block_of(key0)) : block_of(kkey);
+    const uint4* ksrc = kpool + (long long)kblk * blk16 + (kBig ? (key0 & bmask) + k_key : (kkey & bmask));
+#pragma unroll
+    for (int u = 0; u < kKW; ++u) {
+      const int c = w * kKW + u;
+      load_row_to_lds(ksrc + ((long long)c << bshift), &ks[c][0]);
+    }
+#pragma unroll
+    for (int u = 0; u < kVW; ++u) {
+      int j, dh;
+      vrow(u, j, dh);
+      const int key = key0 + j * 8;
+      const int kcv = kBig ? key : (key < Lk ? key : ((Lk - 1) & ~7));
+      const int vblk = kBig ? kblk : __builtin_amdgcn_readfirstlane(block_of(kcv));
+      const uint4* vsrc = vpool + (long long)vblk * blk16 + (long long)((kcv & bmask) >> 3) * kD + dh * 64 + k_key;
+      load_row_to_lds(vsrc, &vs[j][dh * 64]);
+    }
+  };
+  // direct: once tile kt has landed in vs (after a barrier), zero the V values
+  // of keys >= Lk: their weights are 0, but a stale or NaN value would still
+  // poison 0 * v. Only the last tile can hold such keys.
+  auto fix_tail = [&](int kt, uint4 (*vs)[kD]) {
+    const int key0 = kt * kBN;
+    if (key0 + kBN <= Lk) return;
+    for (int e = tid; e < (kBN / 8) * kD; e += kPrefillThreads) {
+      const int j = e / kD, d = e % kD;
+      const int nv = Lk - (key0 + j * 8);            // valid keys of the entry
+      if (nv < 8) {
+        uint4 v = vs[j][d];
+        v.x &= (0 < nv ? 0x0000ffffu : 0u) | (1 < nv ? 0xffff0000u : 0u);
+        v.y &= (2 < nv ? 0x0000ffffu : 0u) | (3 < nv ? 0xffff0000u : 0u);
+        v.z &= (4 < nv ? 0x0000ffffu : 0u) | (5 < nv ? 0xffff0000u : 0u);
+        v.w &= (6 < nv ? 0x0000ffffu : 0u) | (7 < nv ? 0xffff0000u : 0u);
+        vs[j][d] = v;
+      }
+    }
+    __syncthreads();
+  };
+  // staged (fp8): loads into registers ...
+  auto load_tile = [&](int kt) {
     const int key0 = kt * kBN;
     if constexpr (kBig) {
-      const long long base = (long long)ids.k * blk16 + (key0 & bmask);
-      const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(kpool + base);
+      const int blk = __builtin_amdgcn_readfirstlane(block_of(key0));
+      const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(kpool + (long long)blk * blk16 + (key0 & bmask));
 #pragma unroll
-      for (int u = 0; u < kKLoads; ++u) kreg[u] = kb[koff[u]];
-      const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(vpool + (long long)ids.k * blk16 +
+      for (int u = 0; u < kKLoads; ++u)
+        kreg[u] = kb[uint32_t((k_c0 + u * (kPrefillThreads / kBN)) << bshift) + k_key];
+      const u32x4_t* vb = reinterpret_cast<const u32x4_t*>(vpool + (long long)blk * blk16 +
                                                            (long long)((key0 & bmask) / kX) * kD);
 #pragma unroll
-      for (int u = 0; u < kVLoads; ++u) vreg[u] = vb[voff[u]];
-      return;
-    }
-    {
+      for (int u = 0; u < kVLoads; ++u) vreg[u] = vb[uint32_t((v_j0 + u * (kPrefillThreads / kD)) * kD + v_d)];
+    } else {
       const int key = key0 + k_key;
       const int kc = key < Lk ? key : Lk - 1;
-      const uint4* src = kpool + ids.k * blk16 + (kc & bmask);
+      const uint4* src = kpool + (long long)block_of(kc) * blk16 + (kc & bmask);
       // keys past Lk read the last key instead; their scores are masked
 #pragma unroll
       for (int u = 0; u < kKLoads; ++u)
         kreg[u] = reinterpret_cast<const u32x4_t*>(src)[(long long)(k_c0 + u * (kPrefillThreads / kBN)) << bshift];
+#pragma unroll
+      for (int u = 0; u < kVLoads; ++u) {
+        const int j = v_j0 + u * (kPrefillThreads / kD);   // x-key chunk of the tile
+        const int vkey = key0 + j * kX;
+        const int kcv = vkey < Lk ? vkey : ((Lk - 1) & ~(kX - 1));
+        vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[(long long)block_of(kcv) * blk16 +
+                                                          (long long)((kcv & bmask) / kX) * kD + v_d];
+      }
+    }
+  };
+  // ... widened to bf16 and written to LDS (every e4m3 value is a bf16 value);
+  // V values past Lk are zeroed on the bytes first
+  auto store_tile = [&](uint4 (*ks)[kBN], uint4 (*vs)[kD], int kt) {
+#pragma unroll
+    for (int u = 0; u < kKLoads; ++u) {
+      const int c8 = k_c0 + u * (kPrefillThreads / kBN);   // head-dims 16*c8 .. 16*c8+15
+      uint32_t wv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[2 * i] = fp8x2_to_bf16x2<false>(kreg[u][i]);
+        wv[2 * i + 1] = fp8x2_to_bf16x2<true>(kreg[u][i]);
+      }
+      ks[2 * c8][k_key] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      ks[2 * c8 + 1][k_key] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
     }
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      const int j = v_j0 + u * (kPrefillThreads / kD);   // x-key chunk of the tile
-      const int key = key0 + j * kX;
-      const int kc = key < Lk ? key : ((Lk - 1) & ~(kX - 1));
-      vreg[u] = reinterpret_cast<const u32x4_t*>(vpool)[ids.v[kBig ? 0 : u] * blk16 + (long long)((kc & bmask) / kX) * kD + v_d];
-    }
-  };
-  // V values past Lk are zeroed here, where the loads have landed anyway (their
-  // weights are 0, but a stale or NaN value would still poison 0 * v)
-  auto store_tile = [&](int buf, int kt) {
-    if constexpr (!kFp8) {
-#pragma unroll
-      for (int u = 0; u < kKLoads; ++u)
-        k_s[buf][k_c0 + u * (kPrefillThreads / kBN)][k_key] = __builtin_bit_cast(uint4, kreg[u]);
-      if (kt * kBN + kBN > Lk) {
-#pragma unroll
-        for (int u = 0; u < kVLoads; ++u) {
-          const int nv = Lk - (kt * kBN + (v_j0 + u * (kPrefillThreads / kD)) * 8);  // valid keys of the chunk
-          if (nv < 8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              vreg[u][i] &= (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kVLoads; ++u) {
-        const int j = v_j0 + u * (kPrefillThreads / kD);
-        const int step = j >> 1, second = j & 1;   // chunk j holds keys 8j..8j+7 of the tile
-        // keys 0-3 of the chunk go to half 0, keys 4-7 to half 1; first or second 8 bytes
-        reinterpret_cast<uint2*>(&v_s[buf][step][0][v_d])[second] = make_uint2(vreg[u][0], vreg[u][1]);
-        reinterpret_cast<uint2*>(&v_s[buf][step][1][v_d])[second] = make_uint2(vreg[u][2], vreg[u][3]);
-      }
-    } else {
-      // fp8 pool: a 16-byte chunk holds 16 values; converted exactly to bf16 here
-      // (every e4m3 value is a bf16 value), into the same LDS layouts as bf16.
-#pragma unroll
-      for (int u = 0; u < kKLoads; ++u) {
-        const int c8 = k_c0 + u * (kPrefillThreads / kBN);   // head-dims 16*c8 .. 16*c8+15
-        uint32_t w[8];
+      const int step = v_j0 + u * (kPrefillThreads / kD);  // 16-key chunk
+      const int nv = Lk - (kt * kBN + step * 16);           // valid keys of the chunk
+      if (nv < 16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          w[2 * i] = fp8x2_to_bf16x2<false>(kreg[u][i]);
-          w[2 * i + 1] = fp8x2_to_bf16x2<true>(kreg[u][i]);
+          uint32_t mask = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) mask |= (4 * i + b < nv) ? (0xffu << (8 * b)) : 0u;
+          vreg[u][i] &= mask;
         }
-        k_s[buf][2 * c8][k_key] = make_uint4(w[0], w[1], w[2], w[3]);
-        k_s[buf][2 * c8 + 1][k_key] = make_uint4(w[4], w[5], w[6], w[7]);
       }
+      uint32_t wv[8];   // dword i holds keys 4i..4i+3
 #pragma unroll
-      for (int u = 0; u < kVLoads; ++u) {
-        const int step = v_j0 + u * (kPrefillThreads / kD);  // 16-key chunk = one PV step
-        const int nv = Lk - (kt * kBN + step * 16);           // valid keys of the chunk
-        if (nv < 16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t mask = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) mask |= (4 * i + b < nv) ? (0xffu << (8 * b)) : 0u;
-            vreg[u][i] &= mask;
-          }
-        }
-        // dword i holds keys 4i..4i+3: half 0 takes keys {0-3, 8-11}, half 1 {4-7, 12-15}
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          w[2 * i] = fp8x2_to_bf16x2<false>(vreg[u][i]);
-          w[2 * i + 1] = fp8x2_to_bf16x2<true>(vreg[u][i]);
-        }
-        v_s[buf][step][0][v_d] = make_uint4(w[0], w[1], w[4], w[5]);
-        v_s[buf][step][1][v_d] = make_uint4(w[2], w[3], w[6], w[7]);
+      for (int i = 0; i < 4; ++i) {
+        wv[2 * i] = fp8x2_to_bf16x2<false>(vreg[u][i]);
+        wv[2 * i + 1] = fp8x2_to_bf16x2<true>(vreg[u][i]);
       }
+      vs[2 * step][v_d] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      vs[2 * step + 1][v_d] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
     }
   };
 
@@ -321,135 +361,164 @@ void prefill_kernel(const PrefillArgs a) {
   }
   const float sc = kFp8 ? a.scale_log2 * a.k_scale[hk] : a.scale_log2;
 
-  // Software pipeline over 64-key tiles: tile kt+1 sits in registers while tile
-  // kt is computed from LDS; after the products it is written to the other LDS
-  // buffer and the loads of tile kt+2 are issued, so every load has a whole
-  // iteration to land before its LDS write (block ids one iteration earlier).
-  TileIds ids;
+  // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T, from LDS buffers kc / vc
+  auto compute_tile = [&](int kt, const uint4 (*kc)[kBN], const uint4 (*vc)[kD]) {
+    const int key0 = kt * kBN;
+    // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
+    f32x16_t sacc[2][kNB];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8_t af = as_bf16x8(kc[ks * 2 + half][mb * 32 + l32]);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(qf[nb][ks]),
+                                                                 sacc[mb][nb], 0, 0, 0);
+      }
+    }
+#if PA_PREFILL_QK_LEAD
+    // keep PA_PREFILL_QK_LEAD fragment reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_QK_LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * kKS - PA_PREFILL_QK_LEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kNB * PA_PREFILL_QK_LEAD, 0);
+#endif
+    // ---- online softmax per query column; build P^T in the B-operand layout.
+    // Scores stay unscaled until one fma + exp2 per element. The reference max
+    // m of a column only moves when the tile's max exceeds it by more than 8
+    // (log2 units), so weights stay <= 2^8 and O, l are rescaled rarely; O and
+    // l share the reference, so the normalised result is unchanged.
+    uint4 pf[kNB][4];   // [nb][16-key step]
+    const bool diag_tile = key0 + kBN - 1 > wave_lim_min;  // some column masks keys here
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      if (diag_tile) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+            if (key > lim[nb]) sacc[mb][nb][i] = -INFINITY;
+          }
+      }
+      float smax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) smax = fmaxf(smax, fmaxf(sacc[mb][nb][i], sacc[mb][nb][i + 1]));
+      smax = pair_max(smax);
+      const float mt = smax * sc;                  // sc > 0: -inf stays -inf
+      const bool grow = mt > m[nb] + 8.f;
+      if (__any(grow)) {
+        const float mn = grow ? mt : m[nb];
+        const float alpha = fast_exp2(m[nb] - mn);  // 0 the first time (O, l are 0)
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
+        m[nb] = mn;
+      }
+      // a column with no admissible key yet keeps m = -inf; its weights are 0
+      const float mneg = m[nb] == -INFINITY ? 0.f : -m[nb];
+      uint32_t packed[2][8];
+      float ps = lsum[nb];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          f32x2_t pp;
+          pp.x = fast_exp2(fmaf(sacc[mb][nb][i], sc, mneg));
+          pp.y = fast_exp2(fmaf(sacc[mb][nb][i + 1], sc, mneg));
+          const bf16x2_t pk = __builtin_convertvector(pp, bf16x2_t);
+          ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnesBf16x2, ps, false);  // sum of the bf16 weights
+          packed[mb][i / 2] = __builtin_bit_cast(uint32_t, pk);
+        }
+      lsum[nb] = ps;
+      // B operand of the 16-key step t = 2*mb + j: accumulator entries 8j .. 8j+7
+      // hold keys {4h..4h+3, 8+4h..8+4h+3} of the step in lane half h; swapping
+      // dwords 2,3 of half 0 with dwords 0,1 of half 1 (v_permlane32_swap) leaves
+      // keys 8h..8h+7 in half h, the order of the V rows in LDS
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const auto r0 = __builtin_amdgcn_permlane32_swap(packed[mb][4 * j], packed[mb][4 * j + 2], false, false);
+          const auto r1 = __builtin_amdgcn_permlane32_swap(packed[mb][4 * j + 1], packed[mb][4 * j + 3], false,
+                                                           false);
+          pf[nb][2 * mb + j] = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+        }
+    }
+    // ---- O^T += V^T P^T; step t covers tile keys 16t + 8h .. 16t + 8h + 7
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int d = db * 32 + l32;
+        const bf16x8_t af = as_bf16x8(vc[2 * t + half][d]);
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb)
+          o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
+                                                              0, 0, 0);
+      }
+    }
+  };
+
+  // Software pipeline over 64-key tiles with two LDS buffers (a, b); the loop
+  // is unrolled by two so that each step names its buffers. Direct (bf16): the
+  // copies of tile kt+1 into the other buffer are issued before tile kt is
+  // computed and waited for at the barrier after it. Staged (fp8): tile kt+1
+  // sits in registers while tile kt is computed; it is written to the other
+  // buffer after the products and the loads of tile kt+2 are issued, so every
+  // load has a whole tile of work to land.
+  auto tile_step = [&](int kt, uint4 (*kc)[kBN], uint4 (*vc)[kD], uint4 (*kn)[kBN], uint4 (*vn)[kD]) {
+    if constexpr (kDirect) {
+      if (kt + 1 < ntiles) {
+        ensure_ids(kt + 1);
+        issue_tile(kt + 1, kn, vn);
+      }
+    } else {
+      if (kt + 2 < ntiles) ensure_ids(kt + 2);
+    }
+    if (kt * kBN <= wave_last) compute_tile(kt, kc, vc);
+    if constexpr (kDirect) {
+      __syncthreads();
+      if (kt + 1 < ntiles) fix_tail(kt + 1, vn);
+    } else {
+      if (kt + 1 < ntiles) store_tile(kn, vn, kt + 1);
+      if (kt + 2 < ntiles) load_tile(kt + 2);
+      __syncthreads();
+    }
+  };
   // the loop sits inside the ntiles > 0 branch so that on every path into it
   // the Q loads are known complete: otherwise the QK^T MFMAs would carry
   // conservative waits on the global loads of the next tile
   if (ntiles > 0) {
-    fetch_ids(0, ids);
-    load_tile(0, ids);
-    store_tile(0, 0);
-    if (ntiles > 1) {
-      fetch_ids(1, ids);
-      load_tile(1, ids);
-    }
-    if (ntiles > 2) fetch_ids(2, ids);
+    load_ids(0);
     __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-      const int buf = kt & 1;
-      const int key0 = kt * kBN;
-      if (key0 <= wave_last) {
-        // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
-        f32x16_t sacc[2][kNB];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const bf16x8_t af = as_bf16x8(k_s[buf][ks * 2 + half][mb * 32 + l32]);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-              sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(qf[nb][ks]),
-                                                                     sacc[mb][nb], 0, 0, 0);
-          }
-        }
-#if PA_PREFILL_QK_LEAD
-        // keep PA_PREFILL_QK_LEAD fragment reads in flight ahead of the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_QK_LEAD, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * kKS - PA_PREFILL_QK_LEAD; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kNB * PA_PREFILL_QK_LEAD, 0);
-#endif
-        // ---- online softmax per query column; build P^T in the B-operand layout.
-        // Scores stay unscaled until one fma + exp2 per element. The reference max
-        // m of a column only moves when the tile's max exceeds it by more than 8
-        // (log2 units), so weights stay <= 2^8 and O, l are rescaled rarely; O and
-        // l share the reference, so the normalised result is unchanged.
-        uint4 pf[kNB][4];   // [nb][16-key step]
-        const bool diag_tile = key0 + kBN - 1 > wave_lim_min;  // some column masks keys here
-#pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) {
-          if (diag_tile) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                if (key > lim[nb]) sacc[mb][nb][i] = -INFINITY;
-              }
-          }
-          float smax = -INFINITY;
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) smax = fmaxf(smax, fmaxf(sacc[mb][nb][i], sacc[mb][nb][i + 1]));
-          smax = pair_max(smax);
-          const float mt = smax * sc;                  // sc > 0: -inf stays -inf
-          const bool grow = mt > m[nb] + 8.f;
-          if (__any(grow)) {
-            const float mn = grow ? mt : m[nb];
-            const float alpha = fast_exp2(m[nb] - mn);  // 0 the first time (O, l are 0)
-            lsum[nb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < kDB; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
-            m[nb] = mn;
-          }
-          // a column with no admissible key yet keeps m = -inf; its weights are 0
-          const float mneg = m[nb] == -INFINITY ? 0.f : -m[nb];
-          uint32_t packed[2][8];
-          float ps = lsum[nb];
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-              f32x2_t pp;
-              pp.x = fast_exp2(fmaf(sacc[mb][nb][i], sc, mneg));
-              pp.y = fast_exp2(fmaf(sacc[mb][nb][i + 1], sc, mneg));
-              const bf16x2_t pk = __builtin_convertvector(pp, bf16x2_t);
-              ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnesBf16x2, ps, false);  // sum of the bf16 weights
-              packed[mb][i / 2] = __builtin_bit_cast(uint32_t, pk);
-            }
-          lsum[nb] = ps;
-          // B operand of the 16-key step t = 2*mb + j: accumulator entries 8j .. 8j+7
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              pf[nb][2 * mb + j] = make_uint4(packed[mb][4 * j], packed[mb][4 * j + 1],
-                                              packed[mb][4 * j + 2], packed[mb][4 * j + 3]);
-        }
-        // ---- O^T += V^T P^T; step t covers tile keys 16t + {4h..4h+3, 8+4h..8+4h+3}
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const int d = db * 32 + l32;
-            const bf16x8_t af = as_bf16x8(v_s[buf][t][half][d]);
-#pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
-              o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, as_bf16x8(pf[nb][t]), o[db][nb],
-                                                                  0, 0, 0);
-          }
-        }
-      }
-      if (kt + 1 < ntiles) store_tile(buf ^ 1, kt + 1);
-      if (kt + 2 < ntiles) load_tile(kt + 2, ids);
-      if (kt + 3 < ntiles) fetch_ids(kt + 3, ids);
+    if constexpr (kDirect) {
+      issue_tile(0, k_a, v_a);
       __syncthreads();
+      fix_tail(0, v_a);
+    } else {
+      load_tile(0);
+      store_tile(k_a, v_a, 0);
+      if (ntiles > 1) load_tile(1);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      tile_step(kt, k_a, v_a, k_b, v_b);
+      if (kt + 1 < ntiles) tile_step(kt + 1, k_b, v_b, k_a, v_a);
     }
   }
 

@@ -78,6 +78,20 @@ def test_prefill_fp8_matches_fp8_decode():
     np.testing.assert_allclose(bf16_f64(host_bits(pre)), dec, rtol=2 ** -7, atol=2e-3)
 
 
+def test_prefill_long_context_small_blocks():
+    """33000 cached keys in 16-token blocks: the workgroup reads more blocks than
+    its in-LDS window of block ids holds, so the window moves during the loop."""
+    for kv in ("bf16", "fp8"):
+        w = W.custom(seed=330, Hq=4, Hkv=1, D=64, bs=16, context_lens=(), prefill=[(33000, 8), (40, 24)],
+                     kv_dtype=kv)
+        case = GpuCase(w)
+        kc, vc = oracle_pools(w)
+        got = bf16_f64(host_bits(case.prefill()))
+        ma, mr = assert_close(got, _oracle_prefill(w, kc, vc), *(TOL if kv == "bf16" else TOL_FP8),
+                              what=f"long small-block prefill {kv}")
+        print(f"[{kv}] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
 def test_mixed_chunked_prefill_workload():
     """Full mixed step: store of 4344 tokens, prefill of the 8 chunks (all rows checked),
     decode of the 248 sequences (all checked)."""
