@@ -214,12 +214,13 @@ void prefill_kernel(const PrefillArgs a) {
     for (int i = tid; i < kIdCache && first + i < nblk; i += kPrefillThreads) ids_s[i] = bt[first + i];
   };
   auto block_of = [&](int key) { return ids_s[(key >> bshift) - wbase]; };
-  // move the window so that it holds every block tile kt reads (uniform branch)
-  auto ensure_ids = [&](int kt) {
-    const int lastk = (kt * kBN + kBN < Lk ? kt * kBN + kBN : Lk) - 1;
+  // move the window so that it holds every block tiles t0..t1 read (uniform
+  // branch; two tiles span at most 8 blocks, far fewer than the window)
+  auto ensure_ids = [&](int t0, int t1) {
+    const int lastk = (t1 * kBN + kBN < Lk ? t1 * kBN + kBN : Lk) - 1;
     if ((lastk >> bshift) - wbase >= kIdCache) {
       __syncthreads();
-      load_ids((kt * kBN) >> bshift);
+      load_ids((t0 * kBN) >> bshift);
       __syncthreads();
     }
   };
@@ -236,24 +237,49 @@ void prefill_kernel(const PrefillArgs a) {
     j = e / (kD / 64);
     dh = e % (kD / 64);
   };
-  // direct: issue the pool -> LDS copies of tile kt into the buffers ks / vs
-  auto issue_tile = [&](int kt, uint4 (*ks)[kBN], uint4 (*vs)[kD]) {
+  // direct: issue the pool -> LDS copies of tile kt's K into ks ...
+  // direct: the block ids a tile's copies need, read from ids_s ahead of the
+  // copies and kept raw in VGPRs so that the LDS read latency is not waited
+  // for: this lane's K row (one id per tile with kBig, which also serves V)
+  // and, with smaller blocks, the wave's V rows
+  struct CopyIds { int k; int v[kBig ? 1 : kVW]; };
+  auto copy_ids = [&](int kt, CopyIds& c) {
+    kt = kt < ntiles ? kt : ntiles - 1;     // past the last tile: ids of the last (unused)
     const int key0 = kt * kBN;
     const int kkey = key0 + k_key < Lk ? key0 + k_key : Lk - 1;
-    const int kblk = kBig ? __builtin_amdgcn_readfirstlane(block_of(key0)) : block_of(kkey);
+    c.k = block_of(kBig ? key0 : kkey);
+    if constexpr (!kBig) {
+#pragma unroll
+      for (int u = 0; u < kVW; ++u) {
+        int j, dh;
+        vrow(u, j, dh);
+        const int key = key0 + j * 8;
+        c.v[u] = block_of(key < Lk ? key : ((Lk - 1) & ~7));
+      }
+    }
+  };
+  auto issue_k = [&](int kt, const CopyIds& ids, uint4 (*ks)[kBN]) {
+    const int key0 = kt * kBN;
+    const int kkey = key0 + k_key < Lk ? key0 + k_key : Lk - 1;
+    const int kblk = kBig ? __builtin_amdgcn_readfirstlane(ids.k) : ids.k;
     const uint4* ksrc = kpool + (long long)kblk * blk16 + (kBig ? (key0 & bmask) + k_key : (kkey & bmask));
 #pragma unroll
     for (int u = 0; u < kKW; ++u) {
       const int c = w * kKW + u;
       load_row_to_lds(ksrc + ((long long)c << bshift), &ks[c][0]);
     }
+  };
+  // ... and of its V into vs
+  auto issue_v = [&](int kt, const CopyIds& ids, uint4 (*vs)[kD]) {
+    const int key0 = kt * kBN;
+    const int vblk0 = __builtin_amdgcn_readfirstlane(ids.k);
 #pragma unroll
     for (int u = 0; u < kVW; ++u) {
       int j, dh;
       vrow(u, j, dh);
       const int key = key0 + j * 8;
       const int kcv = kBig ? key : (key < Lk ? key : ((Lk - 1) & ~7));
-      const int vblk = kBig ? kblk : __builtin_amdgcn_readfirstlane(block_of(kcv));
+      const int vblk = kBig ? vblk0 : __builtin_amdgcn_readfirstlane(ids.v[kBig ? 0 : u]);
       const uint4* vsrc = vpool + (long long)vblk * blk16 + (long long)((kcv & bmask) >> 3) * kD + dh * 64 + k_key;
       load_row_to_lds(vsrc, &vs[j][dh * 64]);
     }
@@ -362,10 +388,9 @@ void prefill_kernel(const PrefillArgs a) {
   const float sc = kFp8 ? a.scale_log2 * a.k_scale[hk] : a.scale_log2;
 
   // ---- one tile: S^T = K Q^T, online softmax, O^T += V^T P^T, from LDS buffers kc / vc
-  auto compute_tile = [&](int kt, const uint4 (*kc)[kBN], const uint4 (*vc)[kD]) {
-    const int key0 = kt * kBN;
-    // ---- S^T = K Q^T  (rows: 64 keys in two blocks of 32; columns: 2 x 32 queries)
-    f32x16_t sacc[2][kNB];
+  // ---- S^T = K Q^T for the tile in kc (rows: 64 keys in two blocks of 32;
+  // columns: this lane's query columns)
+  auto qk_tile = [&](const uint4 (*kc)[kBN], f32x16_t (&sacc)[2][kNB]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -383,22 +408,20 @@ void prefill_kernel(const PrefillArgs a) {
                                                                  sacc[mb][nb], 0, 0, 0);
       }
     }
-#if PA_PREFILL_QK_LEAD
-    // keep PA_PREFILL_QK_LEAD fragment reads in flight ahead of the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_QK_LEAD, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * kKS - PA_PREFILL_QK_LEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kNB * PA_PREFILL_QK_LEAD, 0);
-#endif
+  };
+  // ---- online softmax per query column, in two parts. Scores stay unscaled
+  // until one fma + exp2 per element. The reference max m of a column only
+  // moves when the tile's max exceeds it by more than 8 (log2 units), so
+  // weights stay <= 2^8 and O, l are rescaled rarely; O and l share the
+  // reference, so the normalised result is unchanged.
+  // Part 1: causal mask (diagonal tiles only), column max, move of m.
+  auto softmax_max = [&](int kt, f32x16_t (&sacc)[2][kNB]) {
+    const int key0 = kt * kBN;
     // ---- online softmax per query column; build P^T in the B-operand layout.
     // Scores stay unscaled until one fma + exp2 per element. The reference max
     // m of a column only moves when the tile's max exceeds it by more than 8
     // (log2 units), so weights stay <= 2^8 and O, l are rescaled rarely; O and
     // l share the reference, so the normalised result is unchanged.
-    uint4 pf[kNB][4];   // [nb][16-key step]
     const bool diag_tile = key0 + kBN - 1 > wave_lim_min;  // some column masks keys here
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
@@ -429,6 +452,13 @@ void prefill_kernel(const PrefillArgs a) {
           for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
         m[nb] = mn;
       }
+    }
+  };
+  // Part 2: weights rounded to bf16, their sum, P^T in the B-operand layout.
+  uint4 pf[kNB][4];   // [nb][16-key step]
+  auto softmax_exp = [&](f32x16_t (&sacc)[2][kNB]) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
       // a column with no admissible key yet keeps m = -inf; its weights are 0
       const float mneg = m[nb] == -INFINITY ? 0.f : -m[nb];
       uint32_t packed[2][8];
@@ -459,6 +489,8 @@ void prefill_kernel(const PrefillArgs a) {
           pf[nb][2 * mb + j] = make_uint4(r0[0], r1[0], r0[1], r1[1]);
         }
     }
+  };
+  auto pv_tile = [&](const uint4 (*vc)[kD]) {
     // ---- O^T += V^T P^T; step t covers tile keys 16t + 8h .. 16t + 8h + 7
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -473,32 +505,87 @@ void prefill_kernel(const PrefillArgs a) {
       }
     }
   };
+  // one tile, its steps in order (staged path)
+  auto compute_tile = [&](int kt, const uint4 (*kc)[kBN], const uint4 (*vc)[kD]) {
+    f32x16_t sacc[2][kNB];
+    qk_tile(kc, sacc);
+#if PA_PREFILL_QK_LEAD
+    // keep PA_PREFILL_QK_LEAD fragment reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, PA_PREFILL_QK_LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * kKS - PA_PREFILL_QK_LEAD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kNB * PA_PREFILL_QK_LEAD, 0);
+#endif
+    softmax_max(kt, sacc);
+    softmax_exp(sacc);
+    pv_tile(vc);
+  };
 
-  // Software pipeline over 64-key tiles with two LDS buffers (a, b); the loop
-  // is unrolled by two so that each step names its buffers. Direct (bf16): the
-  // copies of tile kt+1 into the other buffer are issued before tile kt is
-  // computed and waited for at the barrier after it. Staged (fp8): tile kt+1
-  // sits in registers while tile kt is computed; it is written to the other
-  // buffer after the products and the loads of tile kt+2 are issued, so every
-  // load has a whole tile of work to land.
-  auto tile_step = [&](int kt, uint4 (*kc)[kBN], uint4 (*vc)[kD], uint4 (*kn)[kBN], uint4 (*vn)[kD]) {
-    if constexpr (kDirect) {
-      if (kt + 1 < ntiles) {
-        ensure_ids(kt + 1);
-        issue_tile(kt + 1, kn, vn);
-      }
-    } else {
-      if (kt + 2 < ntiles) ensure_ids(kt + 2);
-    }
+  // Staged (fp8) loop: two LDS buffers (a, b), unrolled by two so that each
+  // step names its buffers. Tile kt+1 sits in registers while tile kt is
+  // computed; it is written to the other buffer after the products and the
+  // loads of tile kt+2 are issued, so every load has a whole tile of work to land.
+  auto staged_step = [&](int kt, uint4 (*kc)[kBN], uint4 (*vc)[kD], uint4 (*kn)[kBN], uint4 (*vn)[kD]) {
+    if (kt + 2 < ntiles) ensure_ids(kt + 2, kt + 2);
     if (kt * kBN <= wave_last) compute_tile(kt, kc, vc);
-    if constexpr (kDirect) {
-      __syncthreads();
-      if (kt + 1 < ntiles) fix_tail(kt + 1, vn);
-    } else {
-      if (kt + 1 < ntiles) store_tile(kn, vn, kt + 1);
-      if (kt + 2 < ntiles) load_tile(kt + 2);
-      __syncthreads();
+    if (kt + 1 < ntiles) store_tile(kn, vn, kt + 1);
+    if (kt + 2 < ntiles) load_tile(kt + 2);
+    __syncthreads();
+  };
+  // Direct (bf16) loop, pipelined across tiles inside each wave: step kt runs
+  // the softmax and PV of tile kt and the QK^T of tile kt+1, so the 16 QK^T
+  // MFMAs of the next tile interleave with the softmax arithmetic of this one.
+  // K and V of a tile therefore live in LDS at different times: step kt reads
+  // K(kt+1) and V(kt) and copies K(kt+2) and V(kt+1) into the buffers the
+  // previous step finished with (K(t) in k_a / k_b and V(t) in v_a / v_b by
+  // the parity of t); the barrier at the end of the step waits for the copies.
+  f32x16_t s_a[2][kNB], s_b[2][kNB];
+  CopyIds ids_t1, ids_t2;   // ids of tiles kt+1 and kt+2 at the start of step kt
+  auto pipe_step = [&](int kt, const uint4 (*k_next)[kBN], const uint4 (*v_cur)[kD], uint4 (*k_dst)[kBN],
+                       uint4 (*v_dst)[kD], f32x16_t (&s_cur)[2][kNB], f32x16_t (&s_next)[2][kNB]) {
+    // copies of K(kt+2) and V(kt+1) with ids read one and two steps ago; then
+    // the ids of tile kt+3 for the next step
+    if (kt + 2 < ntiles) issue_k(kt + 2, ids_t2, k_dst);
+    if (kt + 1 < ntiles) issue_v(kt + 1, ids_t1, v_dst);
+    if (kt + 3 < ntiles) ensure_ids(kt + 3, kt + 3);
+    ids_t1 = ids_t2;
+    copy_ids(kt + 3, ids_t2);
+    if (kt * kBN <= wave_last) {
+      softmax_max(kt, s_cur);
+      // the two waves sharing a SIMD come from different workgroups; while this
+      // one issues MFMAs it takes issue priority, so that the matrix pipe stays
+      // fed when both are ready (measured: 5-6 % on the mixed step)
+      __builtin_amdgcn_s_setprio(1);
+      // past the last tile this reads a stale buffer; those scores are never used
+      qk_tile(k_next, s_next);
+      softmax_exp(s_cur);
+      // issue order: a few fragment reads ahead, then each QK^T MFMA followed by
+      // a share of the softmax VALU work and the next fragment read
+      constexpr int kQkMfma = 2 * kKS * kNB, kQkReads = 2 * kKS, kLead = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kQkMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 96 / kQkMfma, 0);
+        if (i < kQkReads - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      pv_tile(v_cur);
+      // PV: V fragment reads kept kLead ahead of their MFMAs
+      constexpr int kPvReads = 4 * kDB;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kPvReads - kLead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kNB * kLead, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
+    __syncthreads();
+    if (kt + 1 < ntiles) fix_tail(kt + 1, v_dst);
   };
   // the loop sits inside the ntiles > 0 branch so that on every path into it
   // the Q loads are known complete: otherwise the QK^T MFMAs would carry
@@ -507,18 +594,28 @@ void prefill_kernel(const PrefillArgs a) {
     load_ids(0);
     __syncthreads();
     if constexpr (kDirect) {
-      issue_tile(0, k_a, v_a);
+      copy_ids(0, ids_t1);
+      issue_k(0, ids_t1, k_a);
+      issue_v(0, ids_t1, v_a);
+      copy_ids(1, ids_t1);
+      if (ntiles > 1) issue_k(1, ids_t1, k_b);
+      copy_ids(2, ids_t2);
       __syncthreads();
       fix_tail(0, v_a);
+      if (0 <= wave_last) qk_tile(k_a, s_a);
+      for (int kt = 0; kt < ntiles; kt += 2) {
+        pipe_step(kt, k_b, v_a, k_a, v_b, s_a, s_b);
+        if (kt + 1 < ntiles) pipe_step(kt + 1, k_a, v_b, k_b, v_a, s_b, s_a);
+      }
     } else {
       load_tile(0);
       store_tile(k_a, v_a, 0);
       if (ntiles > 1) load_tile(1);
       __syncthreads();
-    }
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      tile_step(kt, k_a, v_a, k_b, v_b);
-      if (kt + 1 < ntiles) tile_step(kt + 1, k_b, v_b, k_a, v_a);
+      for (int kt = 0; kt < ntiles; kt += 2) {
+        staged_step(kt, k_a, v_a, k_b, v_b);
+        if (kt + 1 < ntiles) staged_step(kt + 1, k_b, v_b, k_a, v_a);
+      }
     }
   }
 
