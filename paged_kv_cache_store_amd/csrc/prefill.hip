@@ -530,7 +530,11 @@ void prefill_kernel(const PrefillArgs a) {
   // loads of tile kt+2 are issued, so every load has a whole tile of work to land.
   auto staged_step = [&](int kt, uint4 (*kc)[kBN], uint4 (*vc)[kD], uint4 (*kn)[kBN], uint4 (*vn)[kD]) {
     if (kt + 2 < ntiles) ensure_ids(kt + 2, kt + 2);
-    if (kt * kBN <= wave_last) compute_tile(kt, kc, vc);
+    if (kt * kBN <= wave_last) {
+      __builtin_amdgcn_s_setprio(1);   // MFMA issue priority, as in the direct loop
+      compute_tile(kt, kc, vc);
+      __builtin_amdgcn_s_setprio(0);
+    }
     if (kt + 1 < ntiles) store_tile(kn, vn, kt + 1);
     if (kt + 2 < ntiles) load_tile(kt + 2);
     __syncthreads();
