@@ -2,9 +2,10 @@
 """Throughput of the paged KV-cache hot path on one MI355X.
 
 A step is one pass of the path over one synthetic batch, all on one stream:
-  * Qwen3-0.6B-shaped decode layer (the headline workload, default): pa_store_kv
-    of the 256 sequences' newest tokens, then pa_decode over their paged
-    contexts (U[100,1024] tokens, 16 Q / 8 KV heads, head_dim 128, block 256);
+  * Qwen3-0.6B-shaped decode layer (the headline workload, default): the 256
+    sequences' newest tokens stored and their paged contexts attended in one
+    pa_store_decode launch (U[100,1024] tokens, 16 Q / 8 KV heads, head_dim
+    128, block 256); --separate-store times pa_store_kv then pa_decode instead;
   * the mixed chunked-prefill step (--workload 4): pa_store_kv of 4344 new
     tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
     of 248 sequences.
@@ -13,10 +14,12 @@ them as separate calls; both figures are in the line).
 Inputs are resident in HBM before the timed region. `value` is the step's
 algorithmic bytes (unique KV bytes read by decode and prefill, q/out, tables,
 plus the store's reads and writes) divided by the wall time per step. The
-`roofline` object is the dominant call (pa_decode) timed on its own: a HIP
-graph of 10 back-to-back launches replayed between HIP events on the stream it
-runs on (per-call figures of the other calls are taken the same way). `cpu_baseline` times the CPU oracle (numpy float64) on
-a bounded sample of the same workload on this host.
+`roofline` object is the dominant call (the decode launch, with the store when
+fused) timed on its own: a HIP graph of 10 back-to-back launches replayed
+between HIP events on the stream it runs on (per-call figures of the other
+calls, and of the separate store and decode, are taken the same way).
+`cpu_baseline` times the CPU oracle (numpy float64) on a bounded sample of the
+same workload on this host.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 2]
 """
@@ -116,7 +119,7 @@ def decode_traffic():
 
 # ---------------------------------------------------------------- GPU set-up
 class Setup:
-    def __init__(self, w):
+    def __init__(self, w, fused=True):
         import torch
 
         import paged_kv_cache_store_amd as pa
@@ -148,6 +151,17 @@ class Setup:
                         dev_i32(w.fill_slots[lo:hi]), self.kc, self.vc, self.ks, self.vs)
         self.new_k, self.new_v = dev_bf16(w.new_k), dev_bf16(w.new_v)
         self.new_slots = dev_i32(w.new_slots)
+        # a decode-only step stores each sequence's newest token inside the decode
+        # launch (pa_store_decode): one token per sequence, slot -1 where empty
+        self.fused = not w.has_prefill and fused
+        if self.fused:
+            live = np.flatnonzero(w.context_lens > 0)
+            assert live.size == w.new_slots.size
+            k1 = np.zeros((w.num_seqs,) + w.new_k.shape[1:], np.uint16)
+            v1 = np.zeros_like(k1)
+            s1 = np.full(w.num_seqs, -1, np.int32)
+            k1[live], v1[live], s1[live] = w.new_k, w.new_v, w.new_slots
+            self.seq_k, self.seq_v, self.seq_slots = dev_bf16(k1), dev_bf16(v1), dev_i32(s1)
         self.q = dev_bf16(w.q)
         self.bt = dev_i32(w.block_tables)
         self.lens = dev_i32(w.context_lens)
@@ -170,6 +184,12 @@ class Setup:
         self.pa.decode(self.q, self.kc, self.vc, self.bt, self.lens, float(w.scale), w.max_context_len,
                        out=self.out, k_scale=self.ks, v_scale=self.vs, partition_size=self.P,
                        workspace=self.ws)
+
+    def store_decode(self):
+        w = self.w
+        self.pa.decode(self.q, self.kc, self.vc, self.bt, self.lens, float(w.scale), w.max_context_len,
+                       out=self.out, k_scale=self.ks, v_scale=self.vs, partition_size=self.P,
+                       workspace=self.ws, new_k=self.seq_k, new_v=self.seq_v, slot_mapping=self.seq_slots)
 
     def prefill(self):
         w = self.w
@@ -203,10 +223,15 @@ def run_steps(st, steps, warmup, graph=True):
     whole step as a HIP graph and time `steps` replays between two
     synchronisations. Returns (ms per step, per-call ms, ms per eager step)."""
     torch = st.torch
-    calls = [("store", st.store)]
-    if st.w.has_prefill:
-        calls.append(("prefill", st.prefill))
-    calls.append(("decode", st.decode))
+    if st.fused:
+        calls = [("store_decode", st.store_decode)]
+        alone = [("store", st.store), ("decode", st.decode)]   # per-call figures only
+    else:
+        calls = [("store", st.store)]
+        if st.w.has_prefill:
+            calls.append(("prefill", st.prefill))
+        calls.append(("decode", st.decode))
+        alone = []
     for _ in range(warmup):
         for _, f in calls:
             f()
@@ -218,7 +243,7 @@ def run_steps(st, steps, warmup, graph=True):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_eager = (t1 - t0) * 1e3 / steps
-    ms = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4)) for name, f in calls}
+    ms = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4)) for name, f in calls + alone}
     if not graph:
         return ms_eager, ms, ms_eager
 
@@ -347,6 +372,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as individual calls instead of one HIP-graph replay")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="decode-only workloads: pa_store_kv then pa_decode as two calls "
+                         "instead of one pa_store_decode")
     ap.add_argument("--copy-calib", action="store_true",
                     help="time a plain 1 GiB device copy (counter calibration / HBM ceiling) and exit")
     args = ap.parse_args()
@@ -368,11 +396,12 @@ def main():
         w = W.make(number)
         if args.partition_size is not None:
             w.partition_size = args.partition_size
-        st = Setup(w)
+        st = Setup(w, fused=not args.separate_store)
         ms_step, ms, ms_eager = run_steps(st, steps, warmup, graph=not args.eager)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
         res = {"w": w, "ms_step": ms_step, "ms_eager": ms_eager, "ms": ms, "decode_bytes": dec_b,
-               "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P}
+               "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P,
+               "fused": st.fused}
         if w.has_prefill:
             res["prefill_flops"], res["prefill_bytes"] = prefill_work(w)
         del st
@@ -384,7 +413,18 @@ def main():
     w = r["w"]
     step_bytes = r["decode_bytes"] + r["store_bytes"] + r.get("prefill_bytes", 0)
     value = step_bytes / (r["ms_step"] * 1e-3) / 1e12
-    dec_tbs = r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12
+    # the dominant launch: the decode, with the newest tokens' store fused into it
+    # on a decode-only step
+    whole = r["P"] >= w.max_context_len
+    if r["fused"]:
+        dom_name, dom_bytes = "store_decode", r["decode_bytes"] + r["store_bytes"]
+        dom_kernel = ("decode_kernel with the newest tokens' store (pa_store_decode; contexts whole, no reduce)"
+                      if whole else "decode_kernel with the store + decode_reduce_kernel (pa_store_decode)")
+    else:
+        dom_name, dom_bytes = "decode", r["decode_bytes"]
+        dom_kernel = ("decode_kernel (pa_decode; contexts whole, no reduce)" if whole
+                      else "decode_kernel + decode_reduce_kernel (pa_decode)")
+    dec_tbs = dom_bytes / (r["ms"][dom_name] * 1e-3) / 1e12
     line = {
         "metric": "paged-attn decode KV TB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
         "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
@@ -397,13 +437,12 @@ def main():
                                    f"mean {float(w.context_lens.mean()):.1f}",
                    "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU",
                    "launch": "eager calls" if args.eager else "one HIP-graph replay per step"},
-        "roofline": {"bound": "hbm",
-                     "kernel": "decode_kernel (pa_decode; contexts whole, no reduce)" if r["P"] >= w.max_context_len
-                     else "decode_kernel + decode_reduce_kernel (pa_decode)",
+        "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(dec_tbs * 1e3, 2), "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
                      "frac": round(dec_tbs / HBM_PEAK_TBS, 4),
-                     "traffic": decode_traffic() if args.workload == 2 and args.partition_size is None else None,
-                     "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
+                     "traffic": decode_traffic() if (args.workload == 2 and args.partition_size is None
+                                                     and r["fused"]) else None,
+                     "bytes_per_launch": dom_bytes, "ms_per_launch": round(r["ms"][dom_name], 5)},
         "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
         "ms_per_step_eager": round(r["ms_eager"], 5),
     }
@@ -416,6 +455,10 @@ def main():
                    "decode_ms": round(e["ms"]["decode"], 5), "decode_unique_bytes": e["decode_bytes"],
                    "decode_logical_TBps": round(e["decode_logical"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),
                    "store_ms": round(e["ms"]["store"], 5), "partition_size": e["P"]}
+            if "store_decode" in e["ms"]:
+                sd = e["ms"]["store_decode"]
+                ent.update({"store_decode_ms": round(sd, 5),
+                            "store_decode_TBps": round((e["decode_bytes"] + e["store_bytes"]) / (sd * 1e-3) / 1e12, 4)})
             if "prefill" in e["ms"]:
                 tf = e["prefill_flops"] / (e["ms"]["prefill"] * 1e-3) / 1e12
                 ent.update({"prefill_TFLOPs": round(tf, 2), "prefill_ms": round(e["ms"]["prefill"], 5),

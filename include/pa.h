@@ -137,6 +137,32 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* pa_store_decode — pa_store_kv of each sequence's newest token followed by
+ * pa_decode, in one launch (the store and the decode are the two halves of a
+ * decode step: "Nano-vLLM…", 三.1 and 三.3).
+ *   new_k, new_v  device bf16 [num_seqs][num_kv_heads][head_dim]: sequence s's
+ *                 newest token
+ *   slot_mapping  device int32 [num_seqs]: its slot; < 0 or >= num_blocks*block_size
+ *                 skips the write (as in pa_store_kv)
+ *   k_cache, v_cache  written at those slots, and read
+ *   every other argument, the workspace rule and the status codes as in
+ *   pa_decode; NULL new_k / new_v / slot_mapping with num_seqs > 0 -> PA_ERR_NULL.
+ * Result: the pool bytes and the output of pa_store_kv(new_k, new_v,
+ * slot_mapping) followed by pa_decode on the same stream, bit for bit, when
+ * every written slot is either the slot of position context_lens[s]-1 of its
+ * own sequence s (through block_tables) or a slot no sequence reads in this
+ * call; otherwise the output is undefined (a block shared by several sequences
+ * is copied before it is written into). In the first case the kernel takes the
+ * token from registers for that position and writes the pool after its last
+ * read; any other slot is written before the decode reads. */
+pa_status pa_store_decode(const void* q, const void* new_k, const void* new_v,
+                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void* out,
+                          const pa_cache_desc* cache, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* pa_prefill_varlen — causal attention of packed query chunks over their
  * sequences' paged keys (cached prefix plus the chunk itself, already written by
  * pa_store_kv): chunked prefill ("nano-vllm-lite…", 核心技术改进 §2).

@@ -55,9 +55,10 @@ def _load():
     lib.pa_decode_partition_size.argtypes = [I32, I32, I32, I32]
     lib.pa_decode_partition_size.restype = I32
     lib.pa_decode.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
+    lib.pa_store_decode.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
     lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
     lib.pa_add_rmsnorm.argtypes = [P, P, P, I32, I32, F, P, P, P]
-    for name in ("pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_add_rmsnorm"):
+    for name in ("pa_store_kv", "pa_decode", "pa_store_decode", "pa_prefill_varlen", "pa_add_rmsnorm"):
         getattr(lib, name).restype = ctypes.c_int
     I64, PI32, PI64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -189,8 +190,11 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, part
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out=None,
-           k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None):
-    """Paged decode attention; returns out ([S, Hq, D] bf16)."""
+           k_scale=None, v_scale=None, partition_size=0, workspace=None, stream=None,
+           new_k=None, new_v=None, slot_mapping=None):
+    """Paged decode attention; returns out ([S, Hq, D] bf16). With new_k / new_v
+    ([S, Hkv, D] bf16) and slot_mapping ([S] int32) each sequence's newest token
+    is stored in the same launch (pa_store_decode)."""
     desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
     dev = k_cache.device
     _check(q, "q", torch.bfloat16, 3, dev)
@@ -210,6 +214,22 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    fused = new_k is not None or new_v is not None or slot_mapping is not None
+    if fused:
+        for name, t in (("new_k", new_k), ("new_v", new_v)):
+            _check(t, name, torch.bfloat16, 3, dev)
+            if tuple(t.shape) != (S, hkv, d):
+                raise ValueError(f"{name} must be [S, Hkv, D] = {(S, hkv, d)}")
+        _check(slot_mapping, "slot_mapping", torch.int32, 1, dev)
+        if slot_mapping.numel() != S:
+            raise ValueError("slot_mapping must have one slot per sequence")
+        st = library().pa_store_decode(_ptr(q), _ptr(new_k), _ptr(new_v), _ptr(slot_mapping), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(block_tables), mb, _ptr(context_lens), S, hq,
+                                       int(max_context_len), float(scale), _ptr(out), ctypes.byref(desc),
+                                       int(partition_size), _ptr(workspace), wbytes, _stream(stream))
+        if st != 0:
+            raise PaError(st, "pa_store_decode")
+        return out
     st = library().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), mb,
                         _ptr(context_lens), S, hq, int(max_context_len), float(scale), _ptr(out),
                         ctypes.byref(desc), int(partition_size), _ptr(workspace), wbytes,

@@ -118,12 +118,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
   return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
 }
 
-pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t max_context_len, float scale, void* out,
-                    const pa_cache_desc* cache, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// pa_decode and pa_store_decode: the same checks and launch; the second also
+// hands the newest tokens to the decode kernel, which stores them.
+pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, float scale, void* out, const pa_cache_desc* cache,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream, const void* new_k, const void* new_v,
+                      const int32_t* slot_mapping, bool fused) {
   pa::PoolDims dims;
   pa_status st = check_cache(cache, &dims);
   if (st != PA_OK) return st;
@@ -135,6 +140,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!(scale == scale)) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  if (fused && (!new_k || !new_v || !slot_mapping)) return PA_ERR_NULL;
   // the grid covers contexts up to the smaller of the two host bounds
   const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
   const int32_t cap = int32_t(cap_ll < max_context_len ? cap_ll : max_context_len);
@@ -147,7 +153,37 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                                       static_cast<const uint8_t*>(v_cache), block_tables,
                                       max_blocks_per_seq, context_lens, num_seqs, num_q_heads, cap,
                                       scale, static_cast<uint16_t*>(out), dims, cache->k_scale,
-                                      cache->v_scale, P, workspace, stream));
+                                      cache->v_scale, P, workspace, stream,
+                                      fused ? static_cast<const uint16_t*>(new_k) : nullptr,
+                                      fused ? static_cast<const uint16_t*>(new_v) : nullptr,
+                                      fused ? slot_mapping : nullptr,
+                                      fused ? static_cast<uint8_t*>(const_cast<void*>(k_cache)) : nullptr,
+                                      fused ? static_cast<uint8_t*>(const_cast<void*>(v_cache)) : nullptr));
+}
+
+}  // namespace
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, void* out,
+                    const pa_cache_desc* cache, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_q_heads, max_context_len, scale, out, cache, partition_size, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, nullptr, false);
+}
+
+pa_status pa_store_decode(const void* q, const void* new_k, const void* new_v,
+                          const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void* out,
+                          const pa_cache_desc* cache, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_q_heads, max_context_len, scale, out, cache, partition_size, workspace,
+                     workspace_bytes, stream, new_k, new_v, slot_mapping, true);
 }
 
 pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,

@@ -65,13 +65,103 @@ struct DecodeArgs {
   int num_parts;   // NP = ceil(context cap / P)
   int ctx_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
   float scale_log2;
+  // store fused into the decode (nullptr: none): the newest token of sequence s
+  const uint16_t* new_k;   // [num_seqs][num_kv_heads][D]
+  const uint16_t* new_v;
+  const int32_t* new_slots;  // [num_seqs]
+  uint8_t* k_store;        // the pools again, writable
+  uint8_t* v_store;
+  long long num_slots;
 };
 
-template <int kD, int kG, bool kFp8>
+// Inputs that no kernel of this file writes, read through the constant address
+// space: their uniform loads stay scalar loads even in the kernel that also
+// stores into the pools (the fused store), which the compiler cannot prove
+// disjoint from them.
+template <typename T>
+using const_as_ptr = const __attribute__((address_space(4))) T*;
+
+template <typename T>
+__device__ __forceinline__ const_as_ptr<T> as_constant(const T* p) {
+  return (const_as_ptr<T>)p;
+}
+
+// Fused store of the newest token of sequence s, KV head h. The token is kept
+// in LDS in the pool's representation (bf16 bits, or fp8 codes: the nearest
+// E4M3 code of the correctly rounded quotient value / scale, as the store
+// kernel writes them): bytes [0, D·es) hold K, [D·es, 2·D·es) hold V, value
+// order. The wave that reads the newest position takes it from there instead
+// of from the pool, and writes the pool only after its last load: a load of a
+// line this kernel has just partly written is served slowly, so the written
+// lines are never read back within the launch.
+
+// Lanes 0..D/4-1 each load 8 bf16 values (lanes below D/8: K, the rest: V).
+template <int kD>
+__device__ __forceinline__ uint4 load_new_token(const DecodeArgs& a, int s, int h, int lane) {
+  const long long row = ((long long)s * a.num_kv_heads + h) * kD;
+  if (lane >= kD / 4) return make_uint4(0, 0, 0, 0);
+  const uint16_t* src = lane < kD / 8 ? a.new_k + row + lane * 8 : a.new_v + row + (lane - kD / 8) * 8;
+  return *reinterpret_cast<const uint4*>(src);
+}
+
+// ... and put them into LDS in the pool's representation.
+template <int kD, bool kFp8>
+__device__ __forceinline__ void stage_new_token(const DecodeArgs& a, uint4 x, int h, int lane,
+                                                uint8_t* tok_s) {
+  if (lane >= kD / 4) return;
+  if constexpr (!kFp8) {
+    reinterpret_cast<uint4*>(tok_s)[lane] = x;
+  } else {
+    const float sc = lane < kD / 8 ? as_constant(a.k_scale)[h] : as_constant(a.v_scale)[h];
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (e & 1) ? (xw[e >> 1] & 0xffff0000u) : (xw[e >> 1] << 16);
+      out[e >> 2] |= e4m3_encode(__uint_as_float(bits) / sc) << (8 * (e & 3));
+    }
+    reinterpret_cast<uint2*>(tok_s)[lane] = make_uint2(out[0], out[1]);
+  }
+}
+
+// Writes the staged token at its slot: lane c < D/x writes K chunk c (16 bytes),
+// lane l writes V values l and l + 64.
+template <int kD, bool kFp8>
+__device__ __forceinline__ void write_new_token(const DecodeArgs& a, long long slot, int h, int lane,
+                                                const uint8_t* tok_s) {
+  constexpr int kX = kFp8 ? 16 : 8;
+  constexpr int kEs = kFp8 ? 1 : 2;
+  const int bs = a.block_size;
+  const long long b = slot / bs;
+  const int o = int(slot % bs);
+  const long long slab = (b * a.num_kv_heads + h) * (long long)bs * kD;   // elements
+  if (lane < kD / kX) {
+    const long long k_el = slab + ((long long)lane * bs + o) * kX;
+    *reinterpret_cast<uint4*>(a.k_store + k_el * kEs) = reinterpret_cast<const uint4*>(tok_s)[lane];
+  }
+  const long long v_el = slab + (long long)(o / kX) * kD * kX + (o % kX);
+#pragma unroll
+  for (int i = 0; i < kD / kWave; ++i) {
+    const int d = lane + i * kWave;
+    const long long el = v_el + (long long)d * kX;
+    if constexpr (!kFp8)
+      reinterpret_cast<uint16_t*>(a.v_store)[el] = reinterpret_cast<const uint16_t*>(tok_s + kD * kEs)[d];
+    else
+      a.v_store[el] = tok_s[kD + d];
+  }
+}
+
+// Waves per SIMD the compiler must leave room for. Some fused-store variants
+// need a few more registers than the plain ones and would drop to 2 waves;
+// held at 3 they do not spill (fp8 with one query head per KV head would).
+constexpr int decode_min_waves(int g, bool fp8, bool store) {
+  return PA_DECODE_WAVES_PER_EU ? PA_DECODE_WAVES_PER_EU
+                                : (store && g < 8 && !(fp8 && g == 1) ? 3 : 1);
+}
+
+template <int kD, int kG, bool kFp8, bool kStore>
 __global__ __launch_bounds__(kDecodeThreads)
-#if PA_DECODE_WAVES_PER_EU
-__attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES_PER_EU)))
-#endif
+__attribute__((amdgpu_waves_per_eu(decode_min_waves(kG, kFp8, kStore))))
 void decode_kernel(const DecodeArgs a) {
   constexpr int kX = kFp8 ? 16 : 8;       // elements per 16-byte chunk
   constexpr int kKC = kD / kX;            // K chunks per key
@@ -101,7 +191,25 @@ void decode_kernel(const DecodeArgs a) {
   int n = a.context_lens[s];
   n = n < a.ctx_cap ? n : a.ctx_cap;
   const int p0 = part * P;
+  // Fused store: the newest token (position n-1) is handled by the one wave
+  // that reads that position, the wave given the partition's tile holding
+  // n-1 (wave 0 of partition 0 for an empty sequence).
+  __shared__ __attribute__((aligned(16))) uint8_t tok_s[kStore ? 2 * kD * (kFp8 ? 1 : 2) : 16];
+  const int t_new = n > 0 ? (n - 1 - p0) / kTile : -1;   // this partition's tile holding n-1
+  long long slot_new = -1;
+  uint4 tok = make_uint4(0, 0, 0, 0);
+  if constexpr (kStore) {
+    if (part == (n > 0 ? (n - 1) / P : 0) && (n <= 0 ? w == 0 : t_new % kDecodeWaves == w)) {
+      slot_new = as_constant(a.new_slots)[s];
+      if (slot_new >= a.num_slots) slot_new = -1;
+    }
+    if (slot_new >= 0) tok = load_new_token<kD>(a, s, h, lane);
+  }
   if (n <= 0) {
+    if (kStore && slot_new >= 0) {
+      stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
+      write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
+    }
     if (part == 0) {
       for (int i = tid; i < kG * kD; i += kDecodeThreads)
         a.out[((long long)s * a.num_q_heads + h * kG) * kD + i] = 0;
@@ -116,11 +224,12 @@ void decode_kernel(const DecodeArgs a) {
   const int nb = (pend - p0 + bs - 1) / bs;
   const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq + p0 / bs;
   for (int i = tid; i < nb; i += kDecodeThreads) blk_s[i] = bt[i];
+  if (kStore && slot_new >= 0) stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
   if (kDecodeWaves > 1) __syncthreads();
 
-  const uint32_t* qg =
-      reinterpret_cast<const uint32_t*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD);
-  const float sc = kFp8 ? a.scale_log2 * a.k_scale[h] : a.scale_log2;
+  const auto qg = as_constant(
+      reinterpret_cast<const uint32_t*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD));
+  const float sc = kFp8 ? a.scale_log2 * as_constant(a.k_scale)[h] : a.scale_log2;
   const long long slab16 = (long long)bs * kD * (kFp8 ? 1 : 2) / 16;  // 16-byte units per (block, head)
   const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache) + (long long)h * slab16;
   const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache) + (long long)h * slab16;
@@ -139,13 +248,16 @@ void decode_kernel(const DecodeArgs a) {
 
   // ---- loads of one tile: K with lane = key, V with lane = head-dim index.
   // Streaming, read-once data: non-temporal loads.
-  auto load_tile = [&](int t, uint4 (&kr)[kKC], uint4 (&vr)[kVC][kDL]) {
+  auto load_k = [&](int t, uint4 (&kr)[kKC]) {
     const int key0 = p0 + t * kTile;
     const int key = key0 + lane;
     const int rel = (key < pend ? key : pend - 1) - p0;
     const uint4* kp = kbase + blk_s[rel / bs] * blk_stride16 + (rel % bs);
 #pragma unroll
     for (int c = 0; c < kKC; ++c) kr[c] = load_nt(kp + (long long)c * bs);
+  };
+  auto load_v = [&](int t, uint4 (&vr)[kVC][kDL]) {
+    const int key0 = p0 + t * kTile;
 #pragma unroll
     for (int j = 0; j < kVC; ++j) {
       int kk = key0 + j * kX;
@@ -156,8 +268,12 @@ void decode_kernel(const DecodeArgs a) {
       for (int dl = 0; dl < kDL; ++dl) vr[j][dl] = load_nt(vp + lane + dl * kWave);
     }
   };
+  auto load_tile = [&](int t, uint4 (&kr)[kKC], uint4 (&vr)[kVC][kDL]) {
+    load_k(t, kr);
+    load_v(t, vr);
+  };
 
-  auto compute_tile = [&](int t, const uint4 (&kr)[kKC], const uint4 (&vr)[kVC][kDL]) {
+  auto qk_tile = [&](int t, const uint4 (&kr)[kKC]) {
     const int key0 = p0 + t * kTile;
     const bool valid = key0 + lane < pend;
     // ---- scores
@@ -199,7 +315,9 @@ void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- PV
+  };
+  auto pv_tile = [&](int t, const uint4 (&vr)[kVC][kDL]) {
+    const int key0 = p0 + t * kTile;
 #pragma unroll
     for (int j = 0; j < kVC; ++j) {
       const int kk = key0 + j * kX;
@@ -256,11 +374,75 @@ void decode_kernel(const DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
+  auto compute_tile = [&](int t, const uint4 (&kr)[kKC], const uint4 (&vr)[kVC][kDL]) {
+    qk_tile(t, kr);
+    pv_tile(t, vr);
+  };
 
-  for (int t = w; t < ntiles; t += kDecodeWaves) {
+  // The wave holding the newest token takes the tile with position n-1 (the
+  // partition's last) after its other tiles. When the slot is that position's
+  // slot, the wave puts the token into the tile's registers as the pool will
+  // hold it and writes the pool after its last load, so nothing written is
+  // read back in the launch. Any other slot is written as the store kernel
+  // writes it, before the tile is read.
+  const bool has_new = kStore && slot_new >= 0;
+  const int t_end = has_new ? t_new : ntiles;
+  for (int t = w; t < t_end; t += kDecodeWaves) {
     uint4 kr[kKC], vr[kVC][kDL];
     load_tile(t, kr, vr);
     compute_tile(t, kr, vr);
+  }
+  if constexpr (kStore) {
+    if (has_new) {
+      const int r = n - 1 - (p0 + t_new * kTile);     // the token's key index in the tile
+      const long long own = (long long)blk_s[(n - 1 - p0) / bs] * bs + (n - 1) % bs;
+      if (own != slot_new) {
+        write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
+        uint4 kr[kKC], vr[kVC][kDL];
+        load_tile(t_new, kr, vr);
+        compute_tile(t_new, kr, vr);
+      } else {
+        // K and V one after the other, so the tile holds no more registers
+        // than an ordinary one while the token is put in
+        {
+          uint4 kr[kKC];
+          load_k(t_new, kr);
+          const uint4* tk = reinterpret_cast<const uint4*>(tok_s);
+#pragma unroll
+          for (int c = 0; c < kKC; ++c) {
+            const uint4 nk = tk[c];
+            if (lane == r) kr[c] = nk;
+          }
+          qk_tile(t_new, kr);
+        }
+        // V: element r % x of the 16-byte unit of key-chunk r / x, for each d
+        uint4 vr[kVC][kDL];
+        load_v(t_new, vr);
+        constexpr int kEs = kFp8 ? 1 : 2;
+        const int jr = r / kX;
+        const int dw = (r % kX) * kEs / 4;
+        const int sh = ((r % kX) * kEs % 4) * 8;
+        const uint32_t keep = ~((kFp8 ? 0xffu : 0xffffu) << sh);
+#pragma unroll
+        for (int dl = 0; dl < kDL; ++dl) {
+          const int d = lane + dl * kWave;
+          const uint32_t nv = (kFp8 ? uint32_t(tok_s[kD + d])
+                                    : uint32_t(reinterpret_cast<const uint16_t*>(tok_s + 2 * kD)[d])) << sh;
+#pragma unroll
+          for (int j = 0; j < kVC; ++j) {
+            if (j == jr) {
+              uint4& u = vr[j][dl];
+              u.x = dw == 0 ? (u.x & keep) | nv : u.x;
+              u.y = dw == 1 ? (u.y & keep) | nv : u.y;
+              u.z = dw == 2 ? (u.z & keep) | nv : u.z;
+              u.w = dw == 3 ? (u.w & keep) | nv : u.w;
+            }
+          }
+        }
+        pv_tile(t_new, vr);
+        write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
+      }
+    }
   }
 
   // ---- merge the waves
@@ -275,7 +457,7 @@ void decode_kernel(const DecodeArgs a) {
     for (int dl = 0; dl < kDL; ++dl) o_s[w][g][lane + dl * kWave] = acc[g][dl];
   }
   __syncthreads();
-  const float vsc = kFp8 ? a.v_scale[h] : 1.f;
+  const float vsc = kFp8 ? as_constant(a.v_scale)[h] : 1.f;
   for (int i = tid; i < kG * kD; i += kDecodeThreads) {
     const int g = i / kD;
     const int d = i % kD;
@@ -346,7 +528,10 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int n
 
 template <int kD, int kG, bool kFp8>
 static void launch_decode_t(const DecodeArgs& a, unsigned grid, hipStream_t stream) {
-  decode_kernel<kD, kG, kFp8><<<grid, kDecodeThreads, 0, stream>>>(a);
+  if (a.new_slots)
+    decode_kernel<kD, kG, kFp8, true><<<grid, kDecodeThreads, 0, stream>>>(a);
+  else
+    decode_kernel<kD, kG, kFp8, false><<<grid, kDecodeThreads, 0, stream>>>(a);
 }
 
 template <int kD, bool kFp8>
@@ -365,7 +550,9 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
                          const int32_t* context_lens, int num_seqs, int num_q_heads,
                          int max_context_len, float scale, uint16_t* out, const PoolDims& pool,
                          const float* k_scale, const float* v_scale, int partition_size,
-                         void* workspace, hipStream_t stream) {
+                         void* workspace, hipStream_t stream, const uint16_t* new_k,
+                         const uint16_t* new_v, const int32_t* new_slots, uint8_t* k_store,
+                         uint8_t* v_store) {
   if (num_seqs == 0) return hipSuccess;
   const int D = pool.head_dim;
   const int G = num_q_heads / pool.num_kv_heads;
@@ -395,6 +582,12 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
   a.num_parts = NP;
   a.ctx_cap = ctx_cap;
   a.scale_log2 = scale * kLog2e;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slots = new_slots;
+  a.k_store = k_store;
+  a.v_store = v_store;
+  a.num_slots = (long long)pool.num_blocks * pool.block_size;
   const unsigned grid = unsigned((long long)num_seqs * pool.num_kv_heads * NP);
   bool ok;
   if (D == 64)

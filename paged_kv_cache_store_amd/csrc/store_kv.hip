@@ -8,8 +8,9 @@
 // One thread moves one 16-byte chunk of the pool's K layout: 8 bf16 head-dim
 // values of one (token, head) for a bf16 pool, 16 values (read as 32 bytes of
 // bf16 input) for an fp8 pool. K chunks are written whole; V is transposed in
-// the pool (x consecutive tokens per 16 bytes), so each value lands in its own
-// 2-byte (bf16) or 1-byte (fp8) position. Reads of k/v are fully coalesced.
+// the pool (x consecutive tokens per 16 bytes): a bf16 run of 8 batch tokens
+// on the 8 slots of one chunk is written as whole chunks by its first token,
+// any other value lands in its own 2-byte (bf16) or 1-byte (fp8) position.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -43,13 +44,50 @@ __global__ __launch_bounds__(256) void store_kv_kernel(
   const long long v_dst = slab + (long long)(o / kX) * head_dim * kX + (o % kX);
   if constexpr (!kFp8) {
     const uint4 kr = *reinterpret_cast<const uint4*>(k + src);
-    const uint4 vr = *reinterpret_cast<const uint4*>(v + src);
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + k_dst) = kr;
-    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache) + v_dst + (long long)c * kX * kX;
-    const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+    // V: when this token and the 7 after it in the batch fill one V chunk (8
+    // consecutive slots starting at a multiple of 8, as a prefill chunk does),
+    // the run's first token writes the 8 chunks of its head-dims whole; the
+    // others of the run write nothing. Any other token writes its values one
+    // 2-byte position at a time.
+    const int e0 = o % kX;
+    const long long lead = t - e0;
+    bool run = lead >= 0 && lead + kX <= num_tokens;   // wave-uniform: a wave holds one token
+    if (run) {
+      int sv[kX];   // independent loads, compared afterwards
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      vc[e * kX] = uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+      for (int i = 0; i < kX; ++i) sv[i] = slots[lead + i];
+#pragma unroll
+      for (int i = 0; i < kX; ++i) run = run && (long long)sv[i] == slot - e0 + i;
+    }
+    uint16_t* vc = reinterpret_cast<uint16_t*>(v_cache) + v_dst + (long long)c * kX * kX;
+    if (run) {
+      if (e0 == 0) {
+        uint32_t in[kX][4];   // token i of the run: head-dims c*8 .. c*8+7
+#pragma unroll
+        for (int i = 0; i < kX; ++i) {
+          const uint4 r = *reinterpret_cast<const uint4*>(v + src + (long long)i * num_kv_heads * head_dim);
+          in[i][0] = r.x; in[i][1] = r.y; in[i][2] = r.z; in[i][3] = r.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {          // head-dim c*8 + j: tokens 0..7 of the chunk
+          uint32_t w[4];
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = (in[2 * p][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+            const uint32_t hi = (in[2 * p + 1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+            w[p] = lo | (hi << 16);
+          }
+          *reinterpret_cast<uint4*>(vc + j * kX) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    } else {
+      const uint4 vr = *reinterpret_cast<const uint4*>(v + src);
+      const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vc[e * kX] = uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+    }
   } else {
     const float ks = k_scale[h];
     const float vs = v_scale[h];

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = pa.header_functions()
-    assert {"pa_store_kv", "pa_decode", "pa_prefill_varlen", "pa_decode_workspace_size",
+    assert {"pa_store_kv", "pa_decode", "pa_store_decode", "pa_prefill_varlen", "pa_decode_workspace_size",
             "pa_decode_partition_size", "pa_status_string", "pa_last_hip_error", "pa_copy_blocks",
             "pa_bm_create", "pa_bm_add_sequence", "pa_bm_append_token"} <= set(names)
     for n in names:
@@ -73,6 +73,23 @@ def test_decode_validation(lib):
     assert decode(lib, desc(bs=256), maxctx=2048, P=256, ws=FAKE, wsb=need - 1) == WS
     # partition block ids must fit the 256-entry LDS table
     assert decode(lib, desc(bs=16), maxctx=8192, mb=512, P=8192, ws=FAKE, wsb=1 << 30) == UNSUP
+
+
+def store_decode(lib, d, nk=FAKE, nv=FAKE, sm=FAKE, S=4, hq=4, maxctx=100, mb=8, P=0):
+    return lib.pa_store_decode(FAKE, nk, nv, sm, FAKE, FAKE, FAKE, mb, FAKE, S, hq, maxctx, 0.125,
+                               FAKE, ctypes.byref(d) if d is not None else None, P, None, 0, None)
+
+
+def test_store_decode_validation(lib):
+    assert store_decode(lib, None) == NULL
+    assert store_decode(lib, desc(), nk=None) == NULL
+    assert store_decode(lib, desc(), nv=None) == NULL
+    assert store_decode(lib, desc(), sm=None) == NULL
+    assert store_decode(lib, desc(), hq=3) == SHAPE
+    assert store_decode(lib, desc(), P=100) == SHAPE
+    assert store_decode(lib, desc(dtype=1)) == NULL                    # fp8 needs scales
+    assert store_decode(lib, desc(), S=0, nk=None, nv=None, sm=None) == OK
+    assert store_decode(lib, desc(bs=256), maxctx=2048, P=256) == WS
 
 
 def test_workspace_and_partition_rules(lib):

@@ -236,6 +236,116 @@ def test_store_skips_negative_and_out_of_range_slots():
     assert np.array_equal(host_bits(case.v_cache), before_v)
 
 
+def test_store_runs_of_slots_bit_exact():
+    """Batches mixing whole aligned runs of 8 slots (written as whole V chunks), an
+    unaligned partial run, a run broken by token order, a run holding an invalid
+    slot and a run cut by the end of the batch: every pool byte equals the oracle's."""
+    import paged_kv_cache_store_amd as pa
+    for kv in ("bf16", "fp8"):
+        w = W.custom(seed=208, Hq=4, Hkv=2, D=64, bs=16, context_lens=(), num_blocks=12, kv_dtype=kv)
+        run = list(range(16, 32))                        # two aligned runs
+        part = list(range(37, 43))                       # unaligned partial run
+        swapped = list(range(48, 56))
+        swapped[3], swapped[4] = swapped[4], swapped[3]  # same slots, order broken
+        holed = list(range(64, 72))
+        holed[5] = -1                                    # a skipped slot inside a run
+        tail = list(range(80, 86))                       # run cut by the end of the batch
+        slots = np.array(run + part + swapped + holed + [176, 177] + tail, dtype=np.int32)
+        T = slots.size
+        rng = np.random.default_rng(9)
+        k = W.f32_to_bf16_bits(rng.standard_normal((T, 2, 64)).astype(np.float32))
+        v = W.f32_to_bf16_bits(rng.standard_normal((T, 2, 64)).astype(np.float32))
+        case = GpuCase(w, store_new=False)
+        kc, vc = poisoned_pools(w)
+        oracle.cache.store(k, v, slots, kc, vc, w.block_size, w.k_scale, w.v_scale)
+        from tests.gpu_util import dev_bf16, dev_i32
+        case.store(dev_bf16(k), dev_bf16(v), dev_i32(slots))
+        assert np.array_equal(host_bits(case.k_cache), kc), kv
+        assert np.array_equal(host_bits(case.v_cache), vc), kv
+
+
+def _newest_per_sequence(w):
+    """The step's new tokens as pa_store_decode takes them: one per sequence, slot
+    -1 for an empty sequence (decode-only workloads list them in sequence order)."""
+    S = w.q.shape[0]
+    live = np.flatnonzero(w.context_lens > 0)
+    assert live.size == w.new_slots.size
+    k = np.zeros((S,) + w.new_k.shape[1:], np.uint16)
+    v = np.zeros_like(k)
+    slots = np.full(S, -1, np.int32)
+    k[live], v[live], slots[live] = w.new_k, w.new_v, w.new_slots
+    return k, v, slots
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_store_decode_matches_store_then_decode(cfg):
+    """pa_store_decode writes the same pool bytes as pa_store_kv and returns the
+    same output bits as pa_decode after it, for every partition size; the output
+    also meets the oracle's tolerance on its own."""
+    import paged_kv_cache_store_amd as pa
+    from tests.gpu_util import dev_bf16, dev_i32
+    w = W.custom(**cfg)
+    print(f"case {cfg}", flush=True)
+    k, v, slots = _newest_per_sequence(w)
+    two_step = GpuCase(w)
+    fused = GpuCase(w, store_new=False)
+    kd, vd, sd = dev_bf16(k), dev_bf16(v), dev_i32(slots)
+    kc, vc = oracle_pools(w)
+    ref = _oracle_decode(w, kc, vc)
+    for ps in sorted({w.partition_size, 0, 256, 4096}):
+        want = host_bits(two_step.decode(partition_size=ps))
+        got = pa.decode(fused.q, fused.k_cache, fused.v_cache, fused.block_tables, fused.context_lens,
+                        float(w.scale), w.max_context_len, k_scale=fused.k_scale, v_scale=fused.v_scale,
+                        partition_size=ps, new_k=kd, new_v=vd, slot_mapping=sd)
+        got = host_bits(got)
+        assert np.array_equal(got, want), f"P={ps}: fused output differs from store + decode"
+        assert_close(bf16_f64(got), ref, *TOL[w.kv_dtype], what=f"fused P={ps}")
+        _check_pools_equal(fused, kc, vc)
+
+
+def test_store_decode_slot_elsewhere():
+    """A slot that is not the newest position's (here: slots of an unused block)
+    is written as pa_store_kv writes it; pools and output match store + decode."""
+    import paged_kv_cache_store_amd as pa
+    from tests.gpu_util import dev_bf16, dev_i32
+    for kv in ("bf16", "fp8"):
+        w = W.custom(seed=210, Hq=8, Hkv=2, D=128, bs=16, context_lens=(40, 9, 100, 33), kv_dtype=kv)
+        k, v, slots = _newest_per_sequence(w)
+        spare = int(w.unused_blocks[0]) * w.block_size
+        slots[1], slots[3] = spare + 3, spare + 12
+        kd, vd, sd = dev_bf16(k), dev_bf16(v), dev_i32(slots)
+        two_step = GpuCase(w)
+        two_step.store(kd, vd, sd)
+        want = host_bits(two_step.decode())
+        fused = GpuCase(w)
+        got = pa.decode(fused.q, fused.k_cache, fused.v_cache, fused.block_tables, fused.context_lens,
+                        float(w.scale), w.max_context_len, k_scale=fused.k_scale, v_scale=fused.v_scale,
+                        new_k=kd, new_v=vd, slot_mapping=sd)
+        assert np.array_equal(host_bits(got), want), kv
+        assert np.array_equal(host_bits(fused.k_cache), host_bits(two_step.k_cache)), kv
+        assert np.array_equal(host_bits(fused.v_cache), host_bits(two_step.v_cache)), kv
+
+
+def test_store_decode_skips_invalid_slots():
+    """A slot < 0 or past the pool writes nothing; the decode still runs."""
+    import paged_kv_cache_store_amd as pa
+    from tests.gpu_util import dev_bf16, dev_i32
+    w = W.custom(seed=209, Hq=8, Hkv=2, D=128, bs=16, context_lens=(40, 9, 0))
+    k, v, slots = _newest_per_sequence(w)
+    case = GpuCase(w, store_new=False)
+    before_k, before_v = host_bits(case.k_cache), host_bits(case.v_cache)
+    slots[0] = -7
+    slots[1] = w.num_blocks * w.block_size
+    slots[2] = -1
+    out = pa.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                    float(w.scale), w.max_context_len, new_k=dev_bf16(k), new_v=dev_bf16(v),
+                    slot_mapping=dev_i32(slots))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(case.k_cache), before_k)
+    assert np.array_equal(host_bits(case.v_cache), before_v)
+    assert not np.any(bf16_f64(host_bits(out))[2])          # empty sequence: zeros
+
+
 def test_wrapper_rejects_bad_arguments():
     import paged_kv_cache_store_amd as pa
     w = W.custom(seed=207, Hq=4, Hkv=2, D=64, bs=16, context_lens=(5,))
