@@ -90,6 +90,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// maximum of three floats in one instruction. fmaxf would first quiet possible
+// signalling NaNs of the MFMA results (one extra instruction per operand); the
+// scores here are never NaN once masked (keys past the context are masked first)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // 16 bytes per lane from global memory into LDS at lds_row + 16 * lane
 // (global_load_lds: the data skips the registers; the wave's lanes land in
 // lane order). Plain void pointers: with the vector-struct pointer types the
@@ -438,7 +447,7 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) smax = fmaxf(smax, fmaxf(sacc[mb][nb][i], sacc[mb][nb][i + 1]));
+        for (int i = 0; i < 16; i += 2) smax = max3f(smax, sacc[mb][nb][i], sacc[mb][nb][i + 1]);
       smax = pair_max(smax);
       const float mt = smax * sc;                  // sc > 0: -inf stays -inf
       const bool grow = mt > m[nb] + 8.f;
