@@ -122,6 +122,52 @@ def test_qwen3_06b_decode_all_sequences(qwen3_06b):
     print(f"[qwen3-0.6b decode] max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
+def _fused_case(w):
+    """Pools holding the cached context only, and the step's newest tokens as
+    pa_store_decode takes them."""
+    from tests.gpu_util import dev_bf16, dev_i32
+    case = GpuCase(w, store_new=False)
+    k, v, slots = _newest_per_sequence(w)
+    return case, dev_bf16(k), dev_bf16(v), dev_i32(slots)
+
+
+def _store_decode(case, k, v, slots, partition_size=None):
+    w = case.w
+    ps = w.partition_size if partition_size is None else partition_size
+    return case.pa.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                          float(w.scale), w.max_context_len, k_scale=case.k_scale, v_scale=case.v_scale,
+                          partition_size=ps, new_k=k, new_v=v, slot_mapping=slots)
+
+
+def test_qwen3_06b_store_decode_full():
+    """The headline step as timed: pa_store_decode over the Qwen3-0.6B layer, every
+    sequence against the oracle, every pool byte against the oracle's store."""
+    w = W.make(2)
+    case, k, v, slots = _fused_case(w)
+    got = bf16_f64(host_bits(_store_decode(case, k, v, slots)))
+    kc, vc = oracle_pools(w)
+    _check_pools_equal(case, kc, vc)
+    ma, mr = assert_close(got, _oracle_decode(w, kc, vc), *TOL["bf16"], what="qwen3-0.6b fused")
+    print(f"[qwen3-0.6b store+decode] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+@pytest.mark.parametrize("number", [3, 5], ids=["qwen3-8b", "fp8-long"])
+def test_store_decode_full_size_matches_two_launches(number):
+    """Qwen3-8B (shared prefix, split contexts) and fp8 long context: the fused
+    call gives the bits of pa_store_kv + pa_decode, output and pools."""
+    w = W.make(number)
+    print(w.name, flush=True)
+    fused, k, v, slots = _fused_case(w)
+    got = host_bits(_store_decode(fused, k, v, slots))
+    fk, fv = host_bits(fused.k_cache), host_bits(fused.v_cache)
+    del fused
+    torch.cuda.empty_cache()
+    two = GpuCase(w)
+    want = host_bits(two.decode())
+    assert np.array_equal(got, want)
+    assert np.array_equal(fk, host_bits(two.k_cache)) and np.array_equal(fv, host_bits(two.v_cache))
+
+
 def test_qwen3_8b_shared_prefix_sampled():
     w = W.make(3)
     case = GpuCase(w)
