@@ -50,6 +50,7 @@ constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kBN = 64;           // keys per tile
 constexpr int kIdCache = 2048;    // block ids held in LDS at a time
+constexpr int kSortMax = 256;     // sequences ranked by length in each workgroup
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -144,10 +145,34 @@ void prefill_kernel(const PrefillArgs a) {
   const int bid = blockIdx.x;
   const int hk = bid % Hkv;
   const int rest = bid / Hkv;
-  // later query blocks and later sequences usually see more keys: start them first
-  const int qb = a.num_qblocks - 1 - rest % a.num_qblocks;
-  const int s = a.num_seqs - 1 - rest / a.num_qblocks;
   const int tid = threadIdx.x;
+  // Longest work first: sequences by decreasing key count (ties by index), and
+  // within a sequence the later query blocks (they see more keys) first. Every
+  // workgroup ranks the sequences itself from cu_k, staged in ids_s (not yet in
+  // use); past kSortMax sequences they are taken in reverse index order.
+  const int qb = a.num_qblocks - 1 - rest % a.num_qblocks;
+  const int want = rest / a.num_qblocks;           // rank of this workgroup's sequence
+  int s = a.num_seqs - 1 - want;
+  if (a.num_seqs > 1 && a.num_seqs <= kSortMax) {
+    const int S = a.num_seqs;
+    for (int i = tid; i < S; i += kPrefillThreads) {
+      const int lk = a.cu_k[i + 1] - a.cu_k[i];
+      ids_s[i] = lk < a.cap_k ? lk : a.cap_k;
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += kPrefillThreads) {
+      const int li = ids_s[i];
+      int rank = 0;
+      for (int j = 0; j < S; ++j) {
+        const int lj = ids_s[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      if (rank == want) ids_s[kIdCache - 1] = i;
+    }
+    __syncthreads();
+    s = ids_s[kIdCache - 1];
+    __syncthreads();                                // ids_s is reused for block ids
+  }
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int l32 = lane % 32;

@@ -43,6 +43,21 @@ def test_prefill_small(cfg):
     print(f"max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
+def test_prefill_equal_lengths_and_many_sequences():
+    """Workgroups take sequences longest first, ties by index: equal-length
+    sequences each get their own workgroups; past the ranked limit (256
+    sequences) they are taken by index. Every row against the oracle."""
+    rng = np.random.default_rng(330)
+    for pf in ([(40, 24)] * 5 + [(0, 64)] * 3 + [(64, 1)],
+               [(int(rng.integers(0, 40)), int(rng.integers(1, 9))) for _ in range(300)]):
+        w = W.custom(seed=331, Hq=4, Hkv=2, D=64, bs=16, context_lens=(), prefill=pf)
+        print(f"{len(pf)} sequences", flush=True)
+        case = GpuCase(w)
+        kc, vc = oracle_pools(w)
+        got = bf16_f64(host_bits(case.prefill()))
+        assert_close(got, _oracle_prefill(w, kc, vc), *TOL, what=f"{len(pf)} sequences")
+
+
 FP8_CASES = [
     dict(seed=321, Hq=4, Hkv=1, D=128, bs=16, prefill=[(0, 1), (0, 17), (0, 64), (0, 65), (16, 16)]),
     dict(seed=322, Hq=8, Hkv=2, D=128, bs=64, prefill=[(100, 30), (37, 200), (0, 300)]),
