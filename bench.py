@@ -444,6 +444,10 @@ def main():
                                                      and r["fused"]) else None,
                      "bytes_per_launch": dom_bytes, "ms_per_launch": round(r["ms"][dom_name], 5)},
         "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
+        # the decode kernel alone (pa_decode, no store), timed the same way
+        "decode_only": {"achieved_GBps": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e9, 2),
+                        "frac": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
+                        "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
         "ms_per_step_eager": round(r["ms_eager"], 5),
     }
     if not args.no_extra:

@@ -641,6 +641,8 @@ void prefill_kernel(const PrefillArgs a) {
       __syncthreads();
       fix_tail(0, v_a);
       if (0 <= wave_last) qk_tile(k_a, s_a);
+      // every wave is done with K(0) before step 0 copies K(2) over it
+      __syncthreads();
       for (int kt = 0; kt < ntiles; kt += 2) {
         pipe_step(kt, k_b, v_a, k_a, v_b, s_a, s_b);
         if (kt + 1 < ntiles) pipe_step(kt + 1, k_a, v_b, k_b, v_a, s_b, s_a);
