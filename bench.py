@@ -379,7 +379,7 @@ def main():
                     help="time a plain 1 GiB device copy (counter calibration / HBM ceiling) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("this build runs on one GPU only: --gpus must be 1 (no multi-GPU path exists)",
+        print("bench.py runs on one GPU only: --gpus must be 1 (no multi-GPU path exists)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -7,7 +7,7 @@ and that PagedAttention only changes where keys/values live
 Both reach the plain result, so this module is the plain result: softmax of
 scale * q.k over the de-paged keys, applied to the de-paged values, in float64.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * query head h reads KV head h // (Hq / Hkv) (grouped-query attention, named
   as a variant on "nano-vllm-lite…", 潜在贡献方向);
 * a decode sequence of context length n attends to positions 0..n-1, its own

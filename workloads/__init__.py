@@ -12,7 +12,7 @@ lengths drawn from 100 to 1024 tokens â€” "DeepSeekå¤åˆ»vLLMåè¶…åŸç‰ˆï¼šAIæ
 section æ€§èƒ½å¯¹å†³; chunked prefill mixed with decode â€” "nano-vllm-liteï¼šæ·±å…¥ç†è§£
 LLMæ¨ç†æœºåˆ¶çš„æ•™è‚²çº§å¼€æºé¡¹ç›®", æ ¸å¿ƒæŠ€æœ¯æ”¹è¿› Â§2; FP8 KV cache â€” same page, Â§3).
 
-Recipe (every reading is listed in the design doc):
+Recipe (each reading of the pages it rests on is stated where it is used):
 * seed = 1000 + workload number; independent sub-streams
   ``default_rng(SeedSequence([seed, k]))`` with k = 0 lengths, 1 block
   permutation, 5 choice of prefix sharers; value draws use
