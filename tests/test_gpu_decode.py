@@ -392,6 +392,53 @@ def test_store_decode_skips_invalid_slots():
     assert not np.any(bf16_f64(host_bits(out))[2])          # empty sequence: zeros
 
 
+def test_store_large_batch_patterns_bit_exact():
+    """A batch large enough for the tiled store path (64 tokens per workgroup):
+    aligned and unaligned runs, runs across a tile edge, order breaks, holes,
+    skipped and out-of-range slots, and scattered single tokens, bf16 and fp8;
+    every pool byte equals the oracle's."""
+    rng = np.random.default_rng(11)
+    for kv in ("bf16", "fp8"):
+        bs, nb = 16, 1400
+        w = W.custom(seed=211, Hq=4, Hkv=2, D=64, bs=bs, context_lens=(), num_blocks=nb, kv_dtype=kv)
+        free = rng.permutation(nb)                 # blocks in random order
+        slots = []
+        for i, blk in enumerate(free[:1100]):
+            base = int(blk) * bs
+            kind = i % 6
+            if kind == 0:                          # whole block in order
+                slots += list(range(base, base + bs))
+            elif kind == 1:                        # unaligned start, partial
+                slots += list(range(base + 3, base + 13))
+            elif kind == 2:                        # order broken inside a run
+                seg = list(range(base, base + bs))
+                seg[5], seg[6] = seg[6], seg[5]
+                slots += seg
+            elif kind == 3:                        # hole (-1) and an out-of-range slot
+                seg = list(range(base, base + bs))
+                seg[2] = -1
+                seg[11] = nb * bs + 7
+                slots += seg
+            elif kind == 4:                        # a few scattered tokens
+                slots += [base + int(o) for o in rng.choice(bs, 3, replace=False)]
+            else:                                  # block in reverse order
+                slots += list(range(base + bs - 1, base - 1, -1))
+        slots = np.array(slots, dtype=np.int32)
+        T = slots.size
+        assert T > 256 * 64 // 2, T                # the tiled path: at least 256 workgroups
+        k = W.f32_to_bf16_bits(rng.standard_normal((T, 2, 64)).astype(np.float32))
+        v = W.f32_to_bf16_bits(rng.standard_normal((T, 2, 64)).astype(np.float32))
+        from tests.gpu_util import dev_bf16, dev_i32
+        case = GpuCase(w, store_new=False)
+        kc, vc = poisoned_pools(w)
+        # the library skips slots past the pool as it skips negative ones
+        oracle.cache.store(k, v, np.where(slots < nb * bs, slots, -1), kc, vc, w.block_size,
+                           w.k_scale, w.v_scale)
+        case.store(dev_bf16(k), dev_bf16(v), dev_i32(slots))
+        assert np.array_equal(host_bits(case.k_cache), kc), kv
+        assert np.array_equal(host_bits(case.v_cache), vc), kv
+
+
 def test_wrapper_rejects_bad_arguments():
     import paged_kv_cache_store_amd as pa
     w = W.custom(seed=207, Hq=4, Hkv=2, D=64, bs=16, context_lens=(5,))
