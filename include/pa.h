@@ -124,7 +124,9 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *   out           device bf16 [num_seqs][num_q_heads][head_dim], fully written
  *   partition_size   0 = automatic, else a multiple of 256 tokens: contexts
  *                 longer than one partition are split and merged by a
- *                 log-sum-exp reduce
+ *                 log-sum-exp reduce. A partition's block ids are staged in
+ *                 a 256-entry table: partition/block_size > 256 is
+ *                 PA_ERR_UNSUPPORTED
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
  *                 (may be NULL when that size is 0); contents on entry ignored
  * Query head h reads KV head h / (num_q_heads / num_kv_heads); the group size
