@@ -82,3 +82,32 @@ def test_norm_inputs_seeded_and_shaped():
     assert x.dtype == r.dtype == w.dtype == np.uint16
     assert np.array_equal(x, x2) and np.array_equal(r, r2) and np.array_equal(w, w2)
     assert not np.array_equal(x, W.norm_inputs(6, 3, 128)[0])
+
+
+def _golden():
+    import os
+    vals = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_workload_values.txt")
+    for line in open(path, encoding="utf-8"):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = (x.strip() for x in line.split("=", 1))
+            vals[k] = [int(t) for t in v.split()]
+    return vals
+
+
+def test_workload_shapes_follow_the_pages():
+    """Sequence counts, length ranges and block sizes printed on the pages
+    (tests/golden/page_workload_values.txt, each value with its citation)."""
+    g = _golden()
+    w2 = W.make(2)
+    assert w2.num_seqs == g["qwen3_06b_num_seqs"][0]
+    assert g["qwen3_06b_len_lo"][0] <= w2.context_lens.min() and w2.context_lens.max() <= g["qwen3_06b_len_hi"][0]
+    w3 = W.make(3)
+    assert w3.num_seqs == g["qwen3_8b_num_seqs"][0]
+    # a decode step's context is an input of 100-1024 tokens plus up to 1024 generated
+    lo, hi = g["qwen3_8b_len_lo"][0], g["qwen3_8b_len_hi"][0]
+    assert lo <= w3.context_lens.min() and w3.context_lens.max() <= 2 * hi
+    for n in (2, 3, 4, 5, 6):
+        assert W.make(n).block_size == g["block_size"][0]
+    assert set(g["block_size_alternatives"]) <= {16, 32, 64, 128, 256}   # all supported
