@@ -107,6 +107,64 @@ def test_prefill_long_context_small_blocks():
         print(f"[{kv}] max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
+def _score_ramp(w, kind, R=12.0, seed=0):
+    """Rewrite the prefill queries and keys so that the scores of a sequence follow
+    `kind` along the key positions: q = u + noise for the G query heads of a KV
+    head, k(p) = r(p) u + noise with u in {-1, +1}^D, so that score(p) is about
+    r(p) sqrt(D) (natural log units) and varies by up to R sqrt(D) log2(e) bits:
+    rise (the maximum keeps moving up), fall (the first keys dominate) or spikes
+    (1 % of the keys at R)."""
+    rng = np.random.default_rng(seed)
+    Hkv, G, D = w.num_kv_heads, w.num_q_heads // w.num_kv_heads, w.head_dim
+    u = rng.choice([-1.0, 1.0], size=(Hkv, D))
+    tq = w.pq.shape[0]
+    q = np.repeat(u, G, axis=0)[None] + 0.25 * rng.standard_normal((tq, w.num_q_heads, D))
+    w.pq = W.f32_to_bf16_bits(q.astype(np.float32))
+    fk = W.bf16_bits_to_f32(w.fill_k).astype(np.float64)
+    nk = W.bf16_bits_to_f32(w.new_k).astype(np.float64)
+    fo = no = 0
+    for i in range(w.cu_seqlens_q.size - 1):
+        chunk = int(w.cu_seqlens_q[i + 1] - w.cu_seqlens_q[i])
+        L = int(w.cu_seqlens_k[i + 1] - w.cu_seqlens_k[i])
+        prefix = L - chunk
+        pos = np.arange(L, dtype=np.float64)
+        if kind == "rise":
+            r = R * pos / max(L - 1, 1)
+        elif kind == "fall":
+            r = R * (1.0 - pos / max(L - 1, 1))
+        else:
+            r = np.where(rng.random(L) < 0.01, R, 0.0)
+        kk = r[:, None, None] * u[None] + 0.25 * rng.standard_normal((L, Hkv, D))
+        fk[fo:fo + prefix] = kk[:prefix]
+        nk[no:no + chunk] = kk[prefix:]
+        fo += prefix
+        no += chunk
+    w.fill_k = W.f32_to_bf16_bits(fk.astype(np.float32))
+    w.new_k = W.f32_to_bf16_bits(nk.astype(np.float32))
+    if w.kv_dtype == "fp8":
+        w.k_scale = W._amax_scale(w.fill_k, w.new_k)
+    return w
+
+
+@pytest.mark.parametrize("kind", ["rise", "fall", "spikes"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_wide_score_range(kind, kv):
+    """Scores spread over ~160 bits along a sequence: the softmax reference has to
+    follow the maximum (exp2 of the raw offsets would overflow fp32), and keys far
+    below it must not disturb the result."""
+    print(f"score ramp {kind} {kv}", flush=True)
+    for cfg in (dict(seed=341, Hq=32, Hkv=8, D=128, bs=256, prefill=[(700, 300), (0, 512), (1500, 40)]),
+                dict(seed=342, Hq=4, Hkv=2, D=64, bs=16, prefill=[(200, 130), (0, 77)])):
+        w = _score_ramp(W.custom(context_lens=(), kv_dtype=kv, **cfg), kind, seed=cfg["seed"])
+        case = GpuCase(w)
+        kc, vc = oracle_pools(w)
+        got = bf16_f64(host_bits(case.prefill()))
+        assert np.isfinite(got).all()
+        ma, mr = assert_close(got, _oracle_prefill(w, kc, vc), *(TOL if kv == "bf16" else TOL_FP8),
+                              what=f"prefill, scores {kind}, {kv}")
+        print(f"[D{w.head_dim} {kind} {kv}] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
 def test_mixed_chunked_prefill_workload():
     """Full mixed step: store of 4344 tokens, prefill of the 8 chunks (all rows checked),
     decode of the 248 sequences (all checked)."""
