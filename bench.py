@@ -10,14 +10,20 @@ A step is one pass of the path over one synthetic batch, all on one stream:
     tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
     of 248 sequences.
 The step's calls are captured once as a HIP graph and replayed (--eager times
-them as separate calls; both figures are in the line).
-Inputs are resident in HBM before the timed region. `value` is the step's
-algorithmic bytes (unique KV bytes read by decode and prefill, q/out, tables,
-plus the store's reads and writes) divided by the wall time per step. The
-`roofline` object is the dominant call (the decode launch, with the store when
-fused) timed on its own: a HIP graph of 10 back-to-back launches replayed
-between HIP events on the stream it runs on (per-call figures of the other
-calls, and of the separate store and decode, are taken the same way).
+them as separate calls).
+Inputs are resident in HBM before the timed region, and the caches are cold:
+before every timed step (and every timed launch of a per-call figure) an
+elementwise kernel reads 512 MiB and writes 512 MiB, four times the 256 MB
+Infinity Cache, so that nothing of the step's working set is served from L2
+or the MALL. That flush is timed on its own and subtracted: a graph of
+[flush, step] and a graph of [flush] are each replayed K times between HIP
+events on the launch stream. `value` is the step's algorithmic bytes (unique KV
+bytes read by decode and prefill, q/out, tables, plus the store's reads and
+writes) divided by the cold time per step. The `roofline` object is the
+dominant call (the decode launch, with the store when fused) timed the same
+way on its own (per-call figures of the other calls, and of the separate store
+and decode, likewise). --warm adds the figures of back-to-back launches with
+warm caches.
 `cpu_baseline` times the CPU oracle (numpy float64) on a bounded sample of the
 same workload on this host.
 
@@ -217,12 +223,57 @@ def time_launches(pa, torch, fn, reps, iters):
     return a.elapsed_time(b) / (reps * iters)
 
 
-def run_steps(st, steps, warmup, graph=True):
-    """Warm up; time `steps` eager steps (wall clock between synchronisations);
-    time each call on its own (time_launches); then, with graph=True, capture one
-    whole step as a HIP graph and time `steps` replays between two
-    synchronisations. Returns (ms per step, per-call ms, ms per eager step)."""
+class Flush:
+    """Evicts L2 and the Infinity Cache (MALL, 256 MB) between timed launches: one
+    elementwise kernel (no memset, capturable) reading 512 MiB and writing 512 MiB."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.torch.add(self.src, 1.0, out=self.dst)
+
+
+def _replay_ms(torch, g, n):
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def cold_launches(pa, torch, fn, flush, reps, iters):
+    """GPU time of one call of fn with cold caches: a HIP graph of `reps` times
+    [flush, fn] and a graph of `reps` flushes, replayed alternately `iters` times
+    each between HIP events on the launch stream; the difference per call."""
+    g1 = pa.capture_step(lambda: [(flush(), fn()) for _ in range(reps)])
+    g0 = pa.capture_step(lambda: [flush() for _ in range(reps)])
+    g1.replay()
+    g0.replay()
+    t1 = t0 = 0.0
+    for _ in range(iters):
+        t1 += _replay_ms(torch, g1, 1)
+        t0 += _replay_ms(torch, g0, 1)
+    del g1, g0
+    return (t1 - t0) / (reps * iters)
+
+
+def run_steps(st, steps, warmup, graph=True, warm=False):
+    """Warm up; time each call on its own with cold caches (cold_launches); then
+    time `steps` whole steps with cold caches: with graph=True one captured HIP
+    graph of [flush, step] replayed `steps` times between HIP events (bracketed
+    by synchronisations), minus the same number of replays of [flush]; with
+    graph=False the calls are issued eagerly, events around each step after its
+    flush. warm=True adds back-to-back (warm-cache) figures. Returns a dict."""
     torch = st.torch
+    flush = Flush(torch)
     if st.fused:
         calls = [("store_decode", st.store_decode)]
         alone = [("store", st.store), ("decode", st.decode)]   # per-call figures only
@@ -232,42 +283,60 @@ def run_steps(st, steps, warmup, graph=True):
             calls.append(("prefill", st.prefill))
         calls.append(("decode", st.decode))
         alone = []
-    for _ in range(warmup):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_eager = (t1 - t0) * 1e3 / steps
-    ms = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4)) for name, f in calls + alone}
-    if not graph:
-        return ms_eager, ms, ms_eager
 
     def step():
         for _, f in calls:
             f()
 
-    g = st.pa.capture_step(step)
     for _ in range(warmup):
-        g.replay()
+        step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, ms, ms_eager
+    out = {"ms": {name: cold_launches(st.pa, torch, f, flush, 10, max(3, steps // 4))
+                  for name, f in calls + alone}}
+    if graph:
+        g1 = st.pa.capture_step(lambda: (flush(), step()))
+        g0 = st.pa.capture_step(flush)
+        for _ in range(warmup):
+            g1.replay()
+        t1 = _replay_ms(torch, g1, steps)      # exactly `steps` steps, each after a flush
+        t0 = _replay_ms(torch, g0, steps)
+        out["ms_step"] = (t1 - t0) / steps
+        del g1, g0
+    else:
+        stream = torch.cuda.current_stream()
+        tot = 0.0
+        for _ in range(steps):
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        out["ms_step"] = tot / steps
+    if warm:
+        out["ms_warm"] = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4))
+                          for name, f in calls + alone}
+        g = st.pa.capture_step(step)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        out["ms_step_warm"] = (time.perf_counter() - t0) * 1e3 / steps
+        del g
+    del flush
+    return out
 
 
 def norm_bench(torch, T, H, steps, warmup):
-    """Time pa_add_rmsnorm (with residual) on [T, H] bf16 rows: a HIP graph of 20
-    launches replayed `steps` times between HIP events on the launch stream.
-    Algorithmic bytes: x and r read, y and the new residual
-    written (4·T·H·2) plus the weight once (H·2)."""
+    """Time pa_add_rmsnorm (with residual) on [T, H] bf16 rows with cold caches
+    (cold_launches: 20 launches per graph, each after a flush). Algorithmic
+    bytes: x and r read, y and the new residual written (4·T·H·2) plus the
+    weight once (H·2)."""
     import paged_kv_cache_store_amd as pa
     import workloads as W
     x, r, w = W.norm_inputs(7, T, H)
@@ -277,25 +346,15 @@ def norm_bench(torch, T, H, steps, warmup):
 
     xd, rd, wd = dev(x), dev(r), dev(w)
     out, hres = torch.empty_like(xd), torch.empty_like(xd)
-    reps = 20          # launches per graph: the small shapes would time the host otherwise
 
-    def launches():
-        for _ in range(reps):
-            pa.add_rmsnorm(xd, wd, 1e-6, residual=rd, out=out, residual_out=hres)
+    def launch():
+        pa.add_rmsnorm(xd, wd, 1e-6, residual=rd, out=out, residual_out=hres)
 
-    g = pa.capture_step(launches)
     for _ in range(warmup):
-        g.replay()
-    stream = torch.cuda.current_stream()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(steps):
-        g.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / (steps * reps)
+        launch()
+    flush = Flush(torch)
+    ms = cold_launches(pa, torch, launch, flush, 20, max(2, steps // 2))
+    del flush
     nbytes = 4 * T * H * 2 + H * 2
     return {"TBps": round(nbytes / (ms * 1e-3) / 1e12, 4), "ms": round(ms, 5), "bytes": nbytes,
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS, 4)}
@@ -375,6 +434,8 @@ def main():
     ap.add_argument("--separate-store", action="store_true",
                     help="decode-only workloads: pa_store_kv then pa_decode as two calls "
                          "instead of one pa_store_decode")
+    ap.add_argument("--warm", action="store_true",
+                    help="also time back-to-back launches with warm caches (context figures)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="time a plain 1 GiB device copy (counter calibration / HBM ceiling) and exit")
     args = ap.parse_args()
@@ -397,9 +458,10 @@ def main():
         if args.partition_size is not None:
             w.partition_size = args.partition_size
         st = Setup(w, fused=not args.separate_store)
-        ms_step, ms, ms_eager = run_steps(st, steps, warmup, graph=not args.eager)
+        t = run_steps(st, steps, warmup, graph=not args.eager, warm=args.warm)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
-        res = {"w": w, "ms_step": ms_step, "ms_eager": ms_eager, "ms": ms, "decode_bytes": dec_b,
+        res = {"w": w, "ms_step": t["ms_step"], "ms": t["ms"], "ms_warm": t.get("ms_warm"),
+               "ms_step_warm": t.get("ms_step_warm"), "decode_bytes": dec_b,
                "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P,
                "fused": st.fused}
         if w.has_prefill:
@@ -436,7 +498,9 @@ def main():
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
                                    f"mean {float(w.context_lens.mean()):.1f}",
                    "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU",
-                   "launch": "eager calls" if args.eager else "one HIP-graph replay per step"},
+                   "launch": "eager calls" if args.eager else "one HIP-graph replay per step",
+                   "caches": "cold (512 MiB read + 512 MiB written before every timed step or launch, "
+                             "timed separately and subtracted)"},
         "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(dec_tbs * 1e3, 2), "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
                      "frac": round(dec_tbs / HBM_PEAK_TBS, 4),
@@ -448,8 +512,14 @@ def main():
         "decode_only": {"achieved_GBps": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e9, 2),
                         "frac": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
                         "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
-        "ms_per_step_eager": round(r["ms_eager"], 5),
     }
+    if args.warm:
+        wdom = r["ms_warm"][dom_name]
+        line["warm"] = {"ms_per_step": round(r["ms_step_warm"], 5),
+                        "value": round(step_bytes / (r["ms_step_warm"] * 1e-3) / 1e12, 4),
+                        "dominant_achieved_GBps": round(dom_bytes / (wdom * 1e-3) / 1e9, 2),
+                        "per_call_ms": {k: round(v, 5) for k, v in r["ms_warm"].items()},
+                        "note": "back-to-back launches, caches warm (context only)"}
     if not args.no_extra:
         extra = {}
         for number in [n for n in (3, 4, 5, 6) if n != args.workload]:
