@@ -68,6 +68,10 @@ typedef enum {
 
 typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
 
+/* Alignment, for every call below: device pointers to bf16 / fp8 data (queries,
+ * keys, values, outputs, pools, workspace) must be 16-byte aligned and int32
+ * arrays 4-byte aligned; anything else is PA_ERR_UNSUPPORTED. */
+
 /* One layer's pool. Supported: block_size in {16,32,64,128,256}, head_dim in
  * {64,128}. For PA_KV_FP8_E4M3, k_scale/v_scale are device float32 arrays of
  * num_kv_heads dequantisation scales (stored byte b means value(b) * scale[h]);
@@ -120,7 +124,7 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                 0 gives a zero output row; values are clamped to
  *                 min(max_context_len, max_blocks_per_seq*block_size)
  *   max_context_len  host bound >= every context_lens[s]; sizes the grid
- *   scale         softmax scale (e.g. 1/sqrt(head_dim))
+ *   scale         softmax scale (e.g. 1/sqrt(head_dim)), finite (else PA_ERR_SHAPE)
  *   out           device bf16 [num_seqs][num_q_heads][head_dim], fully written
  *   partition_size   0 = automatic, else a multiple of 256 tokens: contexts
  *                 longer than one partition are split and merged by a

@@ -41,6 +41,10 @@ pa_status check_cache(const pa_cache_desc* c, pa::PoolDims* dims) {
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+// The kernels move bf16 / fp8 data in 16-byte vectors and read int32 arrays as
+// dwords: data pointers must be 16-byte aligned, int32 arrays 4-byte aligned.
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
 int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
 
 // Automatic partition size. With enough (sequence, query head) rows to fill the
@@ -85,6 +89,9 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
   if (!k_cache || !v_cache) return PA_ERR_NULL;
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 4))
+    return PA_ERR_UNSUPPORTED;
   return hip_status(pa::launch_store_kv(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                                         slot_mapping, num_tokens, static_cast<uint8_t*>(k_cache),
                                         static_cast<uint8_t*>(v_cache), dims, cache->k_scale,
@@ -99,6 +106,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
   if (num_pairs < 0 || num_pairs > 65535) return PA_ERR_SHAPE;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return PA_ERR_NULL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 4)) return PA_ERR_UNSUPPORTED;
   return hip_status(pa::launch_copy_blocks(static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                                            pairs, num_pairs, dims, stream));
 }
@@ -137,10 +145,15 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (num_q_heads % dims.num_kv_heads != 0) return PA_ERR_SHAPE;
   if (!supported_group(num_q_heads / dims.num_kv_heads)) return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || partition_size % 256 != 0) return PA_ERR_SHAPE;
-  if (!(scale == scale)) return PA_ERR_SHAPE;
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
   if (fused && (!new_k || !new_v || !slot_mapping)) return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_UNSUPPORTED;
+  if (fused && (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(slot_mapping, 4)))
+    return PA_ERR_UNSUPPORTED;
   // the grid covers contexts up to the smaller of the two host bounds
   const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
   const int32_t cap = int32_t(cap_ll < max_context_len ? cap_ll : max_context_len);
@@ -204,6 +217,9 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
   if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
     return PA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(block_tables, 4))
+    return PA_ERR_UNSUPPORTED;
   const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
   const int32_t cap_k = int32_t(cap_ll < max_seqlen_k ? cap_ll : max_seqlen_k);
   return hip_status(pa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),

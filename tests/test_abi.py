@@ -64,7 +64,10 @@ def test_decode_validation(lib):
     assert decode(lib, desc(hkv=1), hq=3) == UNSUP            # group 3 not built
     assert decode(lib, desc(), S=-1) == SHAPE
     assert decode(lib, desc(), P=100) == SHAPE                # not a multiple of 256
-    assert decode(lib, desc(), scale=float("nan")) == SHAPE
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert decode(lib, desc(), scale=bad) == SHAPE
+    # any finite scale passes the scale check (q = NULL then fails, so nothing launches)
+    assert decode(lib, desc(), scale=-0.125, q=None) == NULL
     assert decode(lib, desc(), S=0, q=None) == OK             # nothing to do
     # a split decode needs its workspace
     assert decode(lib, desc(bs=256), maxctx=2048, P=256) == WS
@@ -142,3 +145,16 @@ def test_add_rmsnorm_validation(lib):
     assert norm(lib, rout=ctypes.c_void_p(0x2000)) == SHAPE  # residual_out == out
     assert norm(lib, x=ctypes.c_void_p(0x1002)) == UNSUP     # not 16-byte aligned
     assert norm(lib, rout=ctypes.c_void_p(0x3008)) == UNSUP
+
+
+def test_alignment_rules(lib):
+    """bf16 / fp8 data must be 16-byte aligned, int32 arrays 4-byte aligned."""
+    odd16, odd4 = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    assert store(lib, desc(), k=odd16) == UNSUP
+    assert store(lib, desc(), kc=odd16) == UNSUP
+    assert store(lib, desc(), slots=odd4) == UNSUP
+    assert decode(lib, desc(), q=odd16) == UNSUP
+    assert store_decode(lib, desc(), nk=odd16) == UNSUP
+    assert store_decode(lib, desc(), sm=odd4) == UNSUP
+    assert prefill(lib, desc(), q=odd16) == UNSUP
+    assert lib.pa_copy_blocks(odd16, FAKE, FAKE, 1, ctypes.byref(desc()), None) == UNSUP
