@@ -70,7 +70,12 @@ typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
 
 /* Alignment, for every call below: device pointers to bf16 / fp8 data (queries,
  * keys, values, outputs, pools, workspace) must be 16-byte aligned and int32
- * arrays 4-byte aligned; anything else is PA_ERR_UNSUPPORTED. */
+ * arrays 4-byte aligned; anything else is PA_ERR_UNSUPPORTED.
+ * Device-side contents are not validated (that would need a host
+ * synchronisation): every block-table entry a call reads must lie in
+ * [0, num_blocks), and cu_seqlens_q / cu_seqlens_k must be non-decreasing. An
+ * entry outside the pool makes the kernel read outside it. Slots outside the
+ * pool are the one exception: stores skip them. */
 
 /* One layer's pool. Supported: block_size in {16,32,64,128,256}, head_dim in
  * {64,128}. For PA_KV_FP8_E4M3, k_scale/v_scale are device float32 arrays of
