@@ -16,7 +16,7 @@ import re
 
 import torch
 
-__all__ = ["store_kv", "decode", "prefill_varlen", "decode_workspace_size",
+__all__ = ["store_kv", "decode", "prefill_varlen", "add_rmsnorm", "decode_workspace_size",
            "decode_partition_size", "empty_pools", "capture_step", "copy_blocks", "BlockManager",
            "PaError", "LIB_PATH", "library"]
 
@@ -255,6 +255,8 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", torch.bfloat16, 3, dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
     st = library().pa_prefill_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
                                 _ptr(cu_seqlens_k), _ptr(block_tables), block_tables.shape[1], S,
                                 q.shape[1], int(max_seqlen_q), int(max_seqlen_k), float(scale),
