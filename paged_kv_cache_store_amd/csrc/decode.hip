@@ -280,6 +280,37 @@ void decode_kernel(const DecodeArgs a) {
     float sv[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) sv[g] = 0.f;
+    if constexpr (!kStore && kG >= 2) {
+      // One query head at a time. The G heads' 64*G query dwords do not fit in
+      // a wave's SGPRs; held for the whole loop they are spilled to VGPR lanes
+      // and read back every tile (one v_readlane each). Here a head's dwords
+      // are loaded (scalar, from the scalar cache) only after the previous
+      // head's score is known: the address passes through an empty asm that
+      // takes that score, so the loads can neither leave the loop nor all
+      // start at once. (With the fused store the tile loop is in control flow
+      // the compiler treats as divergent, where that asm cannot stay scalar.)
+      uint64_t qa = reinterpret_cast<uint64_t>(qg);
+      int dep = 0;
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        asm volatile("" : "+s"(qa) : "s"(dep));
+        const auto qh = reinterpret_cast<const_as_ptr<uint32_t>>(qa) + g * kQW;
+#pragma unroll
+        for (int c = 0; c < kKC; ++c) {
+          const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (!kFp8) {
+              sv[g] = dot2_bf16(kw[i], qh[c * 4 + i], sv[g]);
+            } else {
+              sv[g] = dot2_bf16(fp8x2_to_bf16x2<false>(kw[i]), qh[c * 8 + 2 * i], sv[g]);
+              sv[g] = dot2_bf16(fp8x2_to_bf16x2<true>(kw[i]), qh[c * 8 + 2 * i + 1], sv[g]);
+            }
+          }
+        }
+        dep = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sv[g]));
+      }
+    } else
 #pragma unroll
     for (int c = 0; c < kKC; ++c) {
       const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
