@@ -188,7 +188,7 @@ void decode_kernel(const DecodeArgs a) {
   const int bs = a.block_size;
   const int P = a.part_size;
 
-  int n = a.context_lens[s];
+  int n = as_constant(a.context_lens)[s];   // scalar load: the tile loop's bounds stay uniform
   n = n < a.ctx_cap ? n : a.ctx_cap;
   const int p0 = part * P;
   // Fused store: the newest token (position n-1) is handled by the one wave
@@ -280,15 +280,15 @@ void decode_kernel(const DecodeArgs a) {
     float sv[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) sv[g] = 0.f;
-    if constexpr (!kStore && kG >= 2) {
+    if constexpr (kG >= 2) {
       // One query head at a time. The G heads' 64*G query dwords do not fit in
       // a wave's SGPRs; held for the whole loop they are spilled to VGPR lanes
       // and read back every tile (one v_readlane each). Here a head's dwords
       // are loaded (scalar, from the scalar cache) only after the previous
       // head's score is known: the address passes through an empty asm that
       // takes that score, so the loads can neither leave the loop nor all
-      // start at once. (With the fused store the tile loop is in control flow
-      // the compiler treats as divergent, where that asm cannot stay scalar.)
+      // start at once. (The asm has to sit in control flow the compiler knows
+      // to be uniform, hence the scalar loads of n and of the newest slot.)
       uint64_t qa = reinterpret_cast<uint64_t>(qg);
       int dep = 0;
 #pragma unroll
@@ -426,7 +426,9 @@ void decode_kernel(const DecodeArgs a) {
   if constexpr (kStore) {
     if (has_new) {
       const int r = n - 1 - (p0 + t_new * kTile);     // the token's key index in the tile
-      const long long own = (long long)blk_s[(n - 1 - p0) / bs] * bs + (n - 1) % bs;
+      // uniform by construction; read as a scalar so that the branches below
+      // stay uniform for the compiler
+      const long long own = (long long)__builtin_amdgcn_readfirstlane(blk_s[(n - 1 - p0) / bs]) * bs + (n - 1) % bs;
       if (own != slot_new) {
         write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
         uint4 kr[kKC], vr[kVC][kDL];
