@@ -22,8 +22,9 @@ bytes read by decode and prefill, q/out, tables, plus the store's reads and
 writes) divided by the cold time per step. The `roofline` object is the
 dominant call (the decode launch, with the store when fused) timed the same
 way on its own (per-call figures of the other calls, and of the separate store
-and decode, likewise). --warm adds the figures of back-to-back launches with
-warm caches.
+and decode, likewise). `ms_per_step_percentiles` (p10/p50/p90) times each
+step on its own, less the median flush. --warm adds the figures of
+back-to-back launches with warm caches.
 `cpu_baseline` times the CPU oracle (numpy float64) on a bounded sample of the
 same workload on this host.
 
@@ -301,10 +302,15 @@ def run_steps(st, steps, warmup, graph=True, warm=False):
         t1 = _replay_ms(torch, g1, steps)      # exactly `steps` steps, each after a flush
         t0 = _replay_ms(torch, g0, steps)
         out["ms_step"] = (t1 - t0) / steps
+        # spread: each replay timed on its own, less the median flush
+        flush_ms = float(np.median([_replay_ms(torch, g0, 1) for _ in range(steps)]))
+        per = np.array([_replay_ms(torch, g1, 1) for _ in range(steps)]) - flush_ms
+        out["step_ms_pct"] = {k: round(float(np.percentile(per, q)), 5)
+                              for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
         del g1, g0
     else:
         stream = torch.cuda.current_stream()
-        tot = 0.0
+        per = []
         for _ in range(steps):
             flush()
             a = torch.cuda.Event(enable_timing=True)
@@ -313,8 +319,10 @@ def run_steps(st, steps, warmup, graph=True, warm=False):
             step()
             b.record(stream)
             torch.cuda.synchronize()
-            tot += a.elapsed_time(b)
-        out["ms_step"] = tot / steps
+            per.append(a.elapsed_time(b))
+        out["ms_step"] = sum(per) / steps
+        out["step_ms_pct"] = {k: round(float(np.percentile(per, q)), 5)
+                              for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     if warm:
         out["ms_warm"] = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4))
                           for name, f in calls + alone}
@@ -460,7 +468,8 @@ def main():
         st = Setup(w, fused=not args.separate_store)
         t = run_steps(st, steps, warmup, graph=not args.eager, warm=args.warm)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
-        res = {"w": w, "ms_step": t["ms_step"], "ms": t["ms"], "ms_warm": t.get("ms_warm"),
+        res = {"w": w, "ms_step": t["ms_step"], "step_ms_pct": t.get("step_ms_pct"), "ms": t["ms"],
+               "ms_warm": t.get("ms_warm"),
                "ms_step_warm": t.get("ms_step_warm"), "decode_bytes": dec_b,
                "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P,
                "fused": st.fused}
@@ -490,7 +499,9 @@ def main():
     line = {
         "metric": "paged-attn decode KV TB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
         "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 5), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 5),
+        # per-step spread (each step timed alone, the median flush subtracted)
+        "ms_per_step_percentiles": r["step_ms_pct"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; bf16 N(0,1) q/k/v, random block permutation)",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
