@@ -524,6 +524,9 @@ def main():
                         "frac": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
                         "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
     }
+    if line["roofline"]["traffic"] is not None:
+        # counter-measured HBM bytes per launch over the algorithmic bytes
+        line["roofline"]["overfetch"] = round(line["roofline"]["traffic"] / dom_bytes, 4)
     if args.warm:
         wdom = r["ms_warm"][dom_name]
         line["warm"] = {"ms_per_step": round(r["ms_step_warm"], 5),
