@@ -2,10 +2,12 @@
 """Throughput of the paged KV-cache hot path on one MI355X.
 
 A step is one pass of the path over one synthetic batch, all on one stream:
-  * Qwen3-0.6B-shaped decode layer (the headline workload, default): the 256
-    sequences' newest tokens stored and their paged contexts attended in one
-    pa_store_decode launch (U[100,1024] tokens, 16 Q / 8 KV heads, head_dim
-    128, block 256); --separate-store times pa_store_kv then pa_decode instead;
+  * the Qwen3-8B-shaped decode layer (the headline workload, default: 1024
+    sequences, U[100,2048] tokens, 32 Q / 8 KV heads, head_dim 128, block 256,
+    307 sequences sharing a 512-token prefix): each sequence's newest token
+    stored and its paged context attended. Both ways of doing that are timed
+    per call: pa_store_kv then pa_decode, and pa_store_decode (the two in one
+    launch); the step uses the faster (--path fused|separate forces one);
   * the mixed chunked-prefill step (--workload 4): pa_store_kv of 4344 new
     tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
     of 248 sequences.
@@ -20,15 +22,19 @@ or the MALL. That flush is timed on its own and subtracted: a graph of
 events on the launch stream. `value` is the step's algorithmic bytes (unique KV
 bytes read by decode and prefill, q/out, tables, plus the store's reads and
 writes) divided by the cold time per step. The `roofline` object is the
-dominant call (the decode launch, with the store when fused) timed the same
-way on its own (per-call figures of the other calls, and of the separate store
-and decode, likewise). `ms_per_step_percentiles` (p10/p50/p90) times each
-step on its own, less the median flush. --warm adds the figures of
-back-to-back launches with warm caches.
-`cpu_baseline` times the CPU oracle (numpy float64) on a bounded sample of the
-same workload on this host.
+dominant launch (the decode kernel; with the store inside it when the step
+uses pa_store_decode) timed the same way on its own; `prefill_roofline` is
+the prefill kernel of the mixed chunked-prefill step against the dense bf16
+MFMA peak. `traffic`, `overfetch` and `mfma_util` are read from the committed
+rocprofv3 counter summaries in profiles/ while the kernel's sources are
+unchanged since they were taken (null otherwise). `ms_per_step_percentiles`
+(p10/p50/p90) times each step on its own, less the median flush. --warm adds
+the figures of back-to-back launches with warm caches.
+`cpu_baseline` times the CPU oracle (numpy float64) on this host: store +
+decode on a bounded sample of the headline workload's sequences, and the
+mixed step's prefill.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3]
 """
 import argparse
 import json
@@ -43,8 +49,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_TBS = 8.0              # MI355X HBM3E, TB/s
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "prefill_mfma_counters.md")
 
 
 def log(*a):
@@ -105,28 +112,43 @@ def prefill_work(w):
     return flops, byts
 
 
-def decode_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, or None when the decode sources changed since it was taken."""
+# The kernel sources each call's counter figures depend on.
+CALL_SOURCES = {"decode": ("decode.hip", "pa_device.h"), "store_decode": ("decode.hip", "pa_device.h"),
+                "prefill": ("prefill.hip", "pa_device.h"), "store": ("store_kv.hip", "pa_device.h")}
+
+
+def sources_sha256(call):
     import hashlib
-    try:
-        text = open(TRAFFIC_PROFILE).read()
-    except OSError:
-        return None
-    fields = dict(line.split(": ", 1) for line in text.splitlines()
-                  if line.startswith(("traffic_bytes_per_launch: ", "decode_source_sha256: ")))
     h = hashlib.sha256()
-    for f in ("decode.hip", "pa_device.h"):       # the sources that define the decode kernel
+    for f in CALL_SOURCES[call]:
         with open(os.path.join(ROOT, "paged_kv_cache_store_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if fields.get("decode_source_sha256", "").strip() != h.hexdigest():
+    return h.hexdigest()
+
+
+def profile_figure(path, name, workload, call):
+    """A counter figure from a committed rocprofv3 summary: the line
+    `<name> w<workload>/<call>: <value>`, used only while the line
+    `sources_sha256 <call>: <hash>` of the same file matches the sources the
+    call's kernel is built from (else None: the kernel changed since)."""
+    try:
+        text = open(path).read()
+    except OSError:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    fields = {}
+    for line in text.splitlines():
+        key, sep, val = line.partition(": ")
+        if sep and (key.startswith(name + " ") or key.startswith("sources_sha256 ")):
+            fields[key.strip()] = val.strip()
+    if fields.get(f"sources_sha256 {call}") != sources_sha256(call):
+        return None
+    val = fields.get(f"{name} w{workload}/{call}")
+    return None if val is None else float(val)
 
 
 # ---------------------------------------------------------------- GPU set-up
 class Setup:
-    def __init__(self, w, fused=True):
+    def __init__(self, w):
         import torch
 
         import paged_kv_cache_store_amd as pa
@@ -158,10 +180,10 @@ class Setup:
                         dev_i32(w.fill_slots[lo:hi]), self.kc, self.vc, self.ks, self.vs)
         self.new_k, self.new_v = dev_bf16(w.new_k), dev_bf16(w.new_v)
         self.new_slots = dev_i32(w.new_slots)
-        # a decode-only step stores each sequence's newest token inside the decode
-        # launch (pa_store_decode): one token per sequence, slot -1 where empty
-        self.fused = not w.has_prefill and fused
-        if self.fused:
+        # a decode-only step may store each sequence's newest token inside the
+        # decode launch (pa_store_decode): one token per sequence, slot -1 where empty
+        self.decode_only = not w.has_prefill
+        if self.decode_only:
             live = np.flatnonzero(w.context_lens > 0)
             assert live.size == w.new_slots.size
             k1 = np.zeros((w.num_seqs,) + w.new_k.shape[1:], np.uint16)
@@ -266,34 +288,46 @@ def cold_launches(pa, torch, fn, flush, reps, iters):
     return (t1 - t0) / (reps * iters)
 
 
-def run_steps(st, steps, warmup, graph=True, warm=False):
-    """Warm up; time each call on its own with cold caches (cold_launches); then
-    time `steps` whole steps with cold caches: with graph=True one captured HIP
-    graph of [flush, step] replayed `steps` times between HIP events (bracketed
-    by synchronisations), minus the same number of replays of [flush]; with
-    graph=False the calls are issued eagerly, events around each step after its
-    flush. warm=True adds back-to-back (warm-cache) figures. Returns a dict."""
+def run_steps(st, steps, warmup, path="auto", graph=True, warm=False):
+    """Warm up; time each call on its own with cold caches (cold_launches); pick
+    the step's calls; then time `steps` whole steps with cold caches: with
+    graph=True one captured HIP graph of [flush, step] replayed `steps` times
+    between HIP events (bracketed by synchronisations), minus the same number of
+    replays of [flush]; with graph=False the calls are issued eagerly, events
+    around each step after its flush. A decode-only step is pa_store_kv +
+    pa_decode ("separate") or pa_store_decode ("fused"); path="auto" takes the
+    one whose per-call figures are faster. warm=True adds back-to-back
+    (warm-cache) figures. Returns a dict."""
     torch = st.torch
     flush = Flush(torch)
-    if st.fused:
-        calls = [("store_decode", st.store_decode)]
-        alone = [("store", st.store), ("decode", st.decode)]   # per-call figures only
+    if st.decode_only:
+        candidates = [("store", st.store), ("decode", st.decode), ("store_decode", st.store_decode)]
     else:
-        calls = [("store", st.store)]
+        candidates = [("store", st.store)]
         if st.w.has_prefill:
-            calls.append(("prefill", st.prefill))
-        calls.append(("decode", st.decode))
-        alone = []
+            candidates.append(("prefill", st.prefill))
+        candidates.append(("decode", st.decode))
+    for _ in range(warmup):
+        for _, f in candidates:
+            f()
+    torch.cuda.synchronize()
+    out = {"ms": {name: cold_launches(st.pa, torch, f, flush, 10, max(3, steps // 4))
+                  for name, f in candidates}}
+    ms = out["ms"]
+    if st.decode_only:
+        if path == "auto":
+            path = "fused" if ms["store_decode"] <= ms["store"] + ms["decode"] else "separate"
+        calls = ([("store_decode", st.store_decode)] if path == "fused"
+                 else [("store", st.store), ("decode", st.decode)])
+    else:
+        path = "separate"
+        calls = candidates
+    out["path"] = path
 
     def step():
         for _, f in calls:
             f()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    out = {"ms": {name: cold_launches(st.pa, torch, f, flush, 10, max(3, steps // 4))
-                  for name, f in calls + alone}}
     if graph:
         g1 = st.pa.capture_step(lambda: (flush(), step()))
         g0 = st.pa.capture_step(flush)
@@ -325,7 +359,7 @@ def run_steps(st, steps, warmup, graph=True, warm=False):
                               for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     if warm:
         out["ms_warm"] = {name: time_launches(st.pa, torch, f, 10, max(2, steps // 4))
-                          for name, f in calls + alone}
+                          for name, f in candidates}
         g = st.pa.capture_step(step)
         for _ in range(warmup):
             g.replay()
@@ -368,21 +402,48 @@ def norm_bench(torch, T, H, steps, warmup):
             "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e12 / HBM_PEAK_TBS, 4)}
 
 
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
-def _oracle_baseline(w, budget_s=12.0):
-    import oracle
+def host_info():
+    """The host the CPU figures come from: usable cores, all cores, CPU model,
+    BLAS threads (numpy's matrix products are the oracle's only threaded part)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        blas = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
+    return {"cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(), "cpu_model": model,
+            "blas_threads": blas}
+
+
+def _oracle_pools(w):
+    import oracle
     ks, vs = oracle.cache.pool_shapes(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
     dt = np.uint8 if w.kv_dtype == "fp8" else np.uint16
     kc, vc = np.zeros(ks, dt), np.zeros(vs, dt)
     oracle.cache.store(w.fill_k, w.fill_v, w.fill_slots, kc, vc, w.block_size, w.k_scale, w.v_scale)
-    done = 0
-    passes = 0
-    nbytes = 0
+    return kc, vc
+
+
+def oracle_decode_baseline(w, budget_s=12.0):
+    """The oracle's store + decode of a decode workload, 16 sequences at a time
+    (each sequence's newest token stored, then its context attended), until
+    about budget_s seconds of work; TB/s over the same algorithmic bytes as the
+    GPU figure. The cached context is stored before timing."""
+    import oracle
+    kc, vc = _oracle_pools(w)
+    done = passes = nbytes = 0
     t_total = 0.0
     while t_total < budget_s and passes < 50:
         chunk = np.arange(done % w.num_seqs, min(w.num_seqs, done % w.num_seqs + 16))
@@ -395,14 +456,46 @@ def _oracle_baseline(w, budget_s=12.0):
         oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.block_size,
                                 w.k_scale, w.v_scale, seqs=chunk)
         t_total += time.perf_counter() - t0
-        nbytes += decode_bytes(w, chunk)[0]
+        nbytes += decode_bytes(w, chunk)[0] + store_bytes_of(w, int(sel.sum()))
         done += len(chunk)
         if done % w.num_seqs == 0:
             passes += 1
-    return {"value": nbytes / t_total / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} sequence decodes ({done / w.num_seqs:.2f} passes over the "
-                      f"{w.num_seqs} sequences of the same workload; store of each newest token + "
-                      f"decode), {t_total:.1f} s of work",
+    return {"value": round(nbytes / t_total / 1e12, 6), "unit": "TB/s", "kind": "oracle",
+            "sample": f"{done} sequence decodes of the {w.name} workload ({done / w.num_seqs:.2f} passes "
+                      f"over its {w.num_seqs} sequences; store of each newest token + decode, float64), "
+                      f"{t_total:.1f} s of work",
+            "seconds": round(t_total, 2), "sequences": done}
+
+
+def store_bytes_of(w, tokens):
+    es = 1 if w.kv_dtype == "fp8" else 2
+    return tokens * w.num_kv_heads * w.head_dim * (2 * 2 + 2 * es) + 4 * tokens
+
+
+def oracle_prefill_baseline(w, budget_s=20.0):
+    """The oracle's prefill of the mixed step's chunks, one sequence at a time
+    until every chunk is done or about budget_s seconds have passed; GFLOP/s
+    over the same algorithmic flops as the GPU figure."""
+    import oracle
+    kc, vc = _oracle_pools(w)
+    oracle.cache.store(w.new_k, w.new_v, w.new_slots, kc, vc, w.block_size, w.k_scale, w.v_scale)
+    t_total = 0.0
+    flops = 0
+    done = 0
+    for s in range(len(w.cu_seqlens_q) - 1):
+        if t_total >= budget_s:
+            break
+        t0 = time.perf_counter()
+        oracle.attention.prefill(w.pq, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.p_block_tables, w.scale,
+                                 w.block_size, w.k_scale, w.v_scale, seqs=[s])
+        t_total += time.perf_counter() - t0
+        lq = int(w.cu_seqlens_q[s + 1] - w.cu_seqlens_q[s])
+        lk = int(w.cu_seqlens_k[s + 1] - w.cu_seqlens_k[s])
+        flops += 4 * w.head_dim * w.num_q_heads * sum(lk - lq + i + 1 for i in range(lq))
+        done += 1
+    return {"value": round(flops / t_total / 1e9, 3), "unit": "GFLOP/s", "kind": "oracle",
+            "sample": f"prefill of {done} of the {len(w.cu_seqlens_q) - 1} chunks of the {w.name} step "
+                      f"(float64), {t_total:.1f} s of work",
             "seconds": round(t_total, 2)}
 
 
@@ -427,21 +520,64 @@ def copy_calibration(torch, reps):
 
 
 # ---------------------------------------------------------------- main
+def tbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e12
+
+
+def decode_entry(r):
+    """Per-call figures of a decode workload: pa_decode alone, pa_store_kv, and
+    (decode-only steps) pa_store_decode against the two separate calls."""
+    ms = r["ms"]
+    ent = {"decode_TBps": round(tbps(r["decode_bytes"], ms["decode"]), 4),
+           "decode_ms": round(ms["decode"], 5), "decode_unique_bytes": r["decode_bytes"],
+           "decode_logical_TBps": round(tbps(r["decode_logical"], ms["decode"]), 4),
+           "store_ms": round(ms["store"], 5), "partition_size": r["P"], "step_path": r["path"],
+           "step_ms": round(r["ms_step"], 5)}
+    if "store_decode" in ms:
+        both = r["decode_bytes"] + r["store_bytes"]
+        ent.update({"store_decode_ms": round(ms["store_decode"], 5),
+                    "store_decode_TBps": round(tbps(both, ms["store_decode"]), 4),
+                    "store_plus_decode_ms": round(ms["store"] + ms["decode"], 5),
+                    "store_plus_decode_TBps": round(tbps(both, ms["store"] + ms["decode"]), 4)})
+    if "prefill" in ms:
+        tf = r["prefill_flops"] / (ms["prefill"] * 1e-3) / 1e12
+        ent.update({"prefill_TFLOPs": round(tf, 2), "prefill_ms": round(ms["prefill"], 5),
+                    "prefill_frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "prefill_flops": r["prefill_flops"]})
+    return ent
+
+
+def prefill_roofline(r):
+    """Roofline object of the prefill kernel of a mixed step (dense bf16 MFMA peak)."""
+    w = r["w"]
+    ms = r["ms"]["prefill"]
+    tf = r["prefill_flops"] / (ms * 1e-3) / 1e12
+    mfma = profile_figure(MFMA_PROFILE, "mfma_util", w.number, "prefill")
+    traffic = profile_figure(TRAFFIC_PROFILE, "traffic_bytes_per_launch", w.number, "prefill")
+    return {"bound": "mfma", "workload": w.name, "kernel": "prefill_kernel (pa_prefill_varlen)",
+            "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": r["prefill_flops"],
+            "ms_per_launch": round(ms, 5), "mfma_util": mfma,
+            "traffic": None if traffic is None else int(traffic),
+            "bytes_per_launch": r["prefill_bytes"],
+            "overfetch": None if traffic is None else round(traffic / r["prefill_bytes"], 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--partition-size", type=int, default=None,
                     help="decode partition size (default: the workload's, else automatic)")
+    ap.add_argument("--path", choices=["auto", "fused", "separate"], default="auto",
+                    help="decode-only steps: pa_store_decode (fused), pa_store_kv + pa_decode "
+                         "(separate), or the faster of the two by their per-call figures (auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
     ap.add_argument("--eager", action="store_true",
                     help="time the step as individual calls instead of one HIP-graph replay")
-    ap.add_argument("--separate-store", action="store_true",
-                    help="decode-only workloads: pa_store_kv then pa_decode as two calls "
-                         "instead of one pa_store_decode")
     ap.add_argument("--warm", action="store_true",
                     help="also time back-to-back launches with warm caches (context figures)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -461,18 +597,17 @@ def main():
         copy_calibration(torch, args.steps)
         return
 
-    def measure(number, steps, warmup):
+    def measure(number, steps, warmup, path):
         w = W.make(number)
         if args.partition_size is not None:
             w.partition_size = args.partition_size
-        st = Setup(w, fused=not args.separate_store)
-        t = run_steps(st, steps, warmup, graph=not args.eager, warm=args.warm)
+        st = Setup(w)
+        t = run_steps(st, steps, warmup, path=path, graph=not args.eager, warm=args.warm)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
         res = {"w": w, "ms_step": t["ms_step"], "step_ms_pct": t.get("step_ms_pct"), "ms": t["ms"],
-               "ms_warm": t.get("ms_warm"),
+               "ms_warm": t.get("ms_warm"), "path": t["path"],
                "ms_step_warm": t.get("ms_step_warm"), "decode_bytes": dec_b,
-               "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P,
-               "fused": st.fused}
+               "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P}
         if w.has_prefill:
             res["prefill_flops"], res["prefill_bytes"] = prefill_work(w)
         del st
@@ -480,14 +615,14 @@ def main():
         return res
 
     log(f"[bench] workload {args.workload}: generating + set-up")
-    r = measure(args.workload, args.steps, args.warmup)
+    r = measure(args.workload, args.steps, args.warmup, args.path)
     w = r["w"]
     step_bytes = r["decode_bytes"] + r["store_bytes"] + r.get("prefill_bytes", 0)
     value = step_bytes / (r["ms_step"] * 1e-3) / 1e12
-    # the dominant launch: the decode, with the newest tokens' store fused into it
-    # on a decode-only step
+    # the dominant launch: the decode kernel, with the newest tokens' store in it
+    # when the step uses pa_store_decode
     whole = r["P"] >= w.max_context_len
-    if r["fused"]:
+    if r["path"] == "fused":
         dom_name, dom_bytes = "store_decode", r["decode_bytes"] + r["store_bytes"]
         dom_kernel = ("decode_kernel with the newest tokens' store (pa_store_decode; contexts whole, no reduce)"
                       if whole else "decode_kernel with the store + decode_reduce_kernel (pa_store_decode)")
@@ -495,38 +630,43 @@ def main():
         dom_name, dom_bytes = "decode", r["decode_bytes"]
         dom_kernel = ("decode_kernel (pa_decode; contexts whole, no reduce)" if whole
                       else "decode_kernel + decode_reduce_kernel (pa_decode)")
-    dec_tbs = dom_bytes / (r["ms"][dom_name] * 1e-3) / 1e12
+    dec_tbs = tbps(dom_bytes, r["ms"][dom_name])
+    traffic = None
+    if args.partition_size is None:
+        traffic = profile_figure(TRAFFIC_PROFILE, "traffic_bytes_per_launch", w.number, dom_name)
     line = {
         "metric": "paged-attn decode KV TB/s (% HBM peak) + prefill TFLOP/s (% MFMA peak)",
         "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 5),
         # per-step spread (each step timed alone, the median flush subtracted)
         "ms_per_step_percentiles": r["step_ms_pct"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; bf16 N(0,1) q/k/v, random block permutation)",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
                                    f"mean {float(w.context_lens.mean()):.1f}",
                    "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU",
+                   "step_path": ("pa_store_decode (store inside the decode launch)" if r["path"] == "fused"
+                                 else "pa_store_kv then pa_decode" + (" (+ pa_prefill_varlen)"
+                                                                      if w.has_prefill else "")),
                    "launch": "eager calls" if args.eager else "one HIP-graph replay per step",
                    "caches": "cold (512 MiB read + 512 MiB written before every timed step or launch, "
                              "timed separately and subtracted)"},
         "roofline": {"bound": "hbm", "kernel": dom_kernel,
                      "achieved": round(dec_tbs * 1e3, 2), "peak": HBM_PEAK_TBS * 1e3, "unit": "GB/s",
                      "frac": round(dec_tbs / HBM_PEAK_TBS, 4),
-                     "traffic": decode_traffic() if (args.workload == 2 and args.partition_size is None
-                                                     and r["fused"]) else None,
+                     "traffic": None if traffic is None else int(traffic),
+                     "overfetch": None if traffic is None else round(traffic / dom_bytes, 4),
                      "bytes_per_launch": dom_bytes, "ms_per_launch": round(r["ms"][dom_name], 5)},
         "per_call_ms": {k: round(v, 5) for k, v in r["ms"].items()},
-        # the decode kernel alone (pa_decode, no store), timed the same way
-        "decode_only": {"achieved_GBps": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e9, 2),
-                        "frac": round(r["decode_bytes"] / (r["ms"]["decode"] * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
-                        "bytes_per_launch": r["decode_bytes"], "ms_per_launch": round(r["ms"]["decode"], 5)},
+        "this_workload": decode_entry(r),
     }
-    if line["roofline"]["traffic"] is not None:
-        # counter-measured HBM bytes per launch over the algorithmic bytes
-        line["roofline"]["overfetch"] = round(line["roofline"]["traffic"] / dom_bytes, 4)
+    if w.number == 3:
+        line["roofline"]["logical_GBps"] = round(tbps(r["decode_logical"], r["ms"]["decode"]) * 1e3, 2)
+    if w.has_prefill:
+        line["prefill_roofline"] = prefill_roofline(r)
     if args.warm:
         wdom = r["ms_warm"][dom_name]
         line["warm"] = {"ms_per_step": round(r["ms_step_warm"], 5),
@@ -534,32 +674,31 @@ def main():
                         "dominant_achieved_GBps": round(dom_bytes / (wdom * 1e-3) / 1e9, 2),
                         "per_call_ms": {k: round(v, 5) for k, v in r["ms_warm"].items()},
                         "note": "back-to-back launches, caches warm (context only)"}
+    w_prefill = w if w.has_prefill else None
     if not args.no_extra:
         extra = {}
-        for number in [n for n in (3, 4, 5, 6) if n != args.workload]:
+        for number in [n for n in (2, 3, 4, 5, 6) if n != args.workload]:
             log(f"[bench] workload {number}")
-            e = measure(number, max(5, args.steps // 2), 2)
-            ent = {"decode_TBps": round(e["decode_bytes"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),
-                   "decode_ms": round(e["ms"]["decode"], 5), "decode_unique_bytes": e["decode_bytes"],
-                   "decode_logical_TBps": round(e["decode_logical"] / (e["ms"]["decode"] * 1e-3) / 1e12, 4),
-                   "store_ms": round(e["ms"]["store"], 5), "partition_size": e["P"]}
-            if "store_decode" in e["ms"]:
-                sd = e["ms"]["store_decode"]
-                ent.update({"store_decode_ms": round(sd, 5),
-                            "store_decode_TBps": round((e["decode_bytes"] + e["store_bytes"]) / (sd * 1e-3) / 1e12, 4)})
-            if "prefill" in e["ms"]:
-                tf = e["prefill_flops"] / (e["ms"]["prefill"] * 1e-3) / 1e12
-                ent.update({"prefill_TFLOPs": round(tf, 2), "prefill_ms": round(e["ms"]["prefill"], 5),
-                            "prefill_frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                            "prefill_flops": e["prefill_flops"]})
-            extra[e["w"].name] = ent
+            e = measure(number, max(5, args.steps // 2), 2, "auto")
+            extra[e["w"].name] = decode_entry(e)
+            if number == 4 and "prefill_roofline" not in line:
+                line["prefill_roofline"] = prefill_roofline(e)
+                w_prefill = e["w"]
+            del e
         for name, (T, H) in W.NORM_WORKLOADS.items():
             log(f"[bench] add_rmsnorm {name}")
             extra["add_rmsnorm: " + name] = norm_bench(torch, T, H, 10, 2)
         line["other_workloads"] = extra
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        line["cpu_baseline"] = _oracle_baseline(w)
+        base = oracle_decode_baseline(w)
+        base.update(host_info())
+        base["threads_note"] = ("one Python thread; numpy's matrix products may use up to "
+                                "blas_threads threads")
+        if w_prefill is not None:
+            log("[bench] CPU oracle prefill baseline")
+            base["prefill"] = oracle_prefill_baseline(w_prefill)
+        line["cpu_baseline"] = base
     print(json.dumps(line), flush=True)
 
 

@@ -58,8 +58,14 @@ def store(k_bits, v_bits, slot_mapping, k_cache, v_cache, block_size,
     v = np.asarray(v_bits)[keep]
     T, H, D = k.shape
     if k_cache.dtype == np.uint8:
-        k = _fp8.quantize(_bf16_to_f32(k), np.asarray(k_scale, np.float32)[None, :, None])
-        v = _fp8.quantize(_bf16_to_f32(v), np.asarray(v_scale, np.float32)[None, :, None])
+        # per KV head h: the code of float32(value) / scale[h] (fp8.quantize,
+        # through its table over the bf16 patterns)
+        kq = np.empty(k.shape, np.uint8)
+        vq = np.empty(v.shape, np.uint8)
+        for h in range(H):
+            kq[:, h] = _fp8.quantize_bf16(k[:, h], np.float32(np.asarray(k_scale, np.float32)[h]))
+            vq[:, h] = _fp8.quantize_bf16(v[:, h], np.float32(np.asarray(v_scale, np.float32)[h]))
+        k, v = kq, vq
     x = _x(k_cache)
     block = slots // block_size
     off = slots % block_size
@@ -81,8 +87,9 @@ def depage(k_cache, v_cache, table_row, length, block_size, k_scale=None, v_scal
     K = k_cache[blocks].transpose(0, 3, 1, 2, 4).reshape(nb * block_size, H, D)[:length]
     V = v_cache[blocks].transpose(0, 2, 4, 1, 3).reshape(nb * block_size, H, D)[:length]
     if k_cache.dtype == np.uint8:
-        K = _fp8.decode(K) * np.asarray(k_scale, np.float32).astype(np.float64)[None, :, None]
-        V = _fp8.decode(V) * np.asarray(v_scale, np.float32).astype(np.float64)[None, :, None]
+        values = _fp8.decode_table()
+        K = values[K] * np.asarray(k_scale, np.float32).astype(np.float64)[None, :, None]
+        V = values[V] * np.asarray(v_scale, np.float32).astype(np.float64)[None, :, None]
     else:
         K = bf16_to_f64(K)
         V = bf16_to_f64(V)

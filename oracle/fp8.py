@@ -61,3 +61,24 @@ def quantize(values_f32, scale_f32) -> np.ndarray:
     the float32 quotient value / scale (IEEE, correctly rounded), then encode."""
     q = np.asarray(values_f32, dtype=np.float32) / np.float32(scale_f32)
     return encode(q.astype(np.float32))
+
+
+def quantize_bf16(bits, scale_f32) -> np.ndarray:
+    """quantize() of bf16 inputs (uint16 bit patterns) with one scale, looked up
+    in a table of quantize() over all 65536 bf16 patterns. quantize() acts on
+    each value alone, so the table gives the same bytes; it only saves the
+    encoding of values that repeat (large pools)."""
+    key = np.float32(scale_f32).tobytes()
+    table = _QUANT_TABLES.get(key)
+    if table is None:
+        every = (np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)).view(np.float32)
+        table = _QUANT_TABLES[key] = quantize(every, np.float32(scale_f32))
+    return table[np.asarray(bits, dtype=np.uint16)]
+
+
+_QUANT_TABLES = {}
+
+
+def decode_table() -> np.ndarray:
+    """decode() of all 256 codes, indexed by code (the same values, looked up)."""
+    return decode(np.arange(256, dtype=np.uint8))

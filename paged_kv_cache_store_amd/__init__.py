@@ -20,8 +20,24 @@ __all__ = ["store_kv", "decode", "prefill_varlen", "add_rmsnorm", "decode_worksp
            "decode_partition_size", "empty_pools", "capture_step", "copy_blocks", "BlockManager",
            "PaError", "LIB_PATH", "library"]
 
-# PA_LIBRARY may point at another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+_IN_TREE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+
+def _library_path():
+    """The in-tree libpa.so. Another build of the same library (a tuning
+    variant) is loaded only when PA_LIBRARY names it and PA_ALLOW_OTHER_LIBRARY=1
+    confirms it; PA_LIBRARY alone is an error, so a stray setting can never
+    swap the library under a run unnoticed."""
+    other = os.environ.get("PA_LIBRARY")
+    if not other:
+        return _IN_TREE
+    if os.environ.get("PA_ALLOW_OTHER_LIBRARY") != "1":
+        raise RuntimeError(f"PA_LIBRARY={other} is set but PA_ALLOW_OTHER_LIBRARY=1 is not: "
+                           f"refusing to load a library other than {_IN_TREE}")
+    return other
+
+
+LIB_PATH = _library_path()
 
 PA_KV_BF16, PA_KV_FP8_E4M3 = 0, 1
 

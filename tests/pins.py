@@ -70,6 +70,19 @@ def pin_fp8_roundtrip():
     assert np.array_equal(oracle.fp8.encode(v[fin].astype(np.float32)), c[fin])
 
 
+def pin_fp8_tables_equal_direct_calls():
+    """The looked-up forms used for large pools give the direct calls' results:
+    every bf16 pattern under several scales, and every code's value."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    f32 = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    for sc in (1.0, 0.0087, 3.5e-3, 1.7, 2.0 ** -10):
+        s = np.float32(sc)
+        assert np.array_equal(oracle.fp8.quantize_bf16(bits, s), oracle.fp8.quantize(f32, s))
+    a = oracle.fp8.decode_table()
+    b = oracle.fp8.decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(a[np.isfinite(b)], b[np.isfinite(b)]) and np.isnan(a[~np.isfinite(b)]).all()
+
+
 # ---------------------------------------------------------------- cache store / depage
 def _small_workloads():
     yield W.custom(seed=11, Hq=4, Hkv=2, D=64, bs=16, context_lens=(1, 16, 17, 40, 0, 33))

@@ -47,3 +47,20 @@ def test_decode_bytes_fp8_and_store_bytes():
     T = w.new_slots.size
     # bf16 k, v read; fp8 codes written; one int32 slot per token
     assert bench.store_bytes(w) == T * w.num_kv_heads * w.head_dim * (2 * 2 + 2 * 1) + 4 * T
+
+
+def test_profile_figures_follow_the_kernel_sources(tmp_path):
+    """Counter figures are read only while the kernel sources they were taken on
+    are unchanged (the hash line of the summary matches)."""
+    p = tmp_path / "summary.md"
+    p.write_text("text\n"
+                 f"sources_sha256 decode: {bench.sources_sha256('decode')}\n"
+                 "traffic_bytes_per_launch w3/decode: 3900000000\n"
+                 "sources_sha256 prefill: 0000\n"
+                 "traffic_bytes_per_launch w4/prefill: 113000000\n")
+    assert bench.profile_figure(str(p), "traffic_bytes_per_launch", 3, "decode") == 3.9e9
+    assert bench.profile_figure(str(p), "traffic_bytes_per_launch", 2, "decode") is None
+    assert bench.profile_figure(str(p), "traffic_bytes_per_launch", 4, "prefill") is None
+    assert bench.profile_figure(str(tmp_path / "missing.md"), "traffic_bytes_per_launch", 3, "decode") is None
+    assert bench.sources_sha256("decode") == bench.sources_sha256("store_decode")
+    assert bench.sources_sha256("decode") != bench.sources_sha256("prefill")

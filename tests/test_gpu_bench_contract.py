@@ -31,8 +31,23 @@ def test_bench_json_line_fields():
         assert key in roof, key
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert d["config"]["step_path"]
     pct = d["ms_per_step_percentiles"]
     assert pct["p10"] <= pct["p50"] <= pct["p90"]
+
+
+def test_bench_prefill_roofline_object():
+    """The mixed chunked-prefill workload carries a prefill roofline against the
+    dense bf16 MFMA peak."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "4", "--steps", "2",
+                        "--warmup", "1", "--no-extra", "--no-cpu-baseline"],
+                       capture_output=True, text=True, timeout=110, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    pr = d["prefill_roofline"]
+    assert pr["bound"] == "mfma" and pr["peak"] == 2500.0 and pr["unit"] == "TFLOP/s"
+    assert 0 < pr["frac"] < 1 and abs(pr["frac"] - pr["achieved"] / pr["peak"]) < 1e-3
+    assert pr["flops_per_launch"] == 77_342_965_760
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -3,7 +3,7 @@
 Store: bit-exact (bf16 bits; fp8 codes) over whole pools, NaN sentinels included.
 Decode: element-wise |gpu - oracle| <= atol + rtol*|oracle| with atol = rtol = 1e-2
 for a bf16 cache and 3e-2 for fp8 (oracle on the same fp8 bytes, float64).
-Full-size workloads are checked on sampled sequences the oracle computes one by one.
+Every workload is checked in full: every sequence's output and every pool byte.
 """
 import math
 
@@ -14,7 +14,8 @@ import torch
 import oracle
 import workloads as W
 from tests.gpu_util import GpuCase, host_bits
-from tests.util import assert_close, bf16_f64, oracle_pools, poisoned_pools, relabel_blocks
+from tests.util import (assert_close, bf16_f64, oracle_decode_threads, oracle_pools, poisoned_pools,
+                        relabel_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,29 +37,6 @@ def _check_pools_equal(case, kc, vc, blocks=None):
     nk = np.count_nonzero(ok_k != rk)
     nv = np.count_nonzero(ok_v != rv)
     assert nk == 0 and nv == 0, f"pool bytes differ: K {nk}, V {nv}"
-
-
-def _seq_blocks(w, seqs):
-    out = set()
-    for s in seqs:
-        out.update(w.block_tables[s, :math.ceil(int(w.context_lens[s]) / w.block_size)].tolist())
-    return np.array(sorted(out), dtype=np.int64)
-
-
-def _oracle_pools_for(w, seqs):
-    """Oracle pools holding only the tokens of the given sequences' blocks."""
-    blocks = _seq_blocks(w, seqs)
-    kc, vc = poisoned_pools(w) if w.num_blocks <= 2048 else _lazy_pools(w)
-    for slots, k, v in ((w.fill_slots, w.fill_k, w.fill_v), (w.new_slots, w.new_k, w.new_v)):
-        sel = np.isin(slots // w.block_size, blocks)
-        oracle.cache.store(k[sel], v[sel], slots[sel], kc, vc, w.block_size, w.k_scale, w.v_scale)
-    return kc, vc, blocks
-
-
-def _lazy_pools(w):
-    ks, vs = oracle.cache.pool_shapes(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.kv_dtype)
-    dt = np.uint8 if w.kv_dtype == "fp8" else np.uint16
-    return np.zeros(ks, dt), np.zeros(vs, dt)
 
 
 # ---------------------------------------------------------------- small workloads, whole pools
@@ -158,10 +136,43 @@ def test_qwen3_06b_store_decode_full():
     print(f"[qwen3-0.6b store+decode] max_abs={ma:.3e} max_rel={mr:.3e}")
 
 
+@pytest.fixture(scope="module", params=[3, 5], ids=["qwen3-8b", "fp8-long"])
+def full_size(request):
+    """Qwen3-8B (1024 sequences, shared prefix) and fp8 long context (64
+    sequences, split contexts): the oracle's pools after storing every cached
+    and new token, and the oracle's decode of every sequence."""
+    w = W.make(request.param)
+    print(w.name, flush=True)
+    kc, vc = oracle_pools(w)
+    ref = oracle_decode_threads(w, kc, vc)
+    return w, kc, vc, ref
+
+
+def test_full_size_store_and_decode_vs_oracle(full_size):
+    """pa_store_kv of every token, then pa_decode: whole pools byte for byte and
+    every sequence's output against the oracle."""
+    w, kc, vc, ref = full_size
+    case = GpuCase(w)
+    _check_pools_equal(case, kc, vc)
+    got = bf16_f64(host_bits(case.decode()))
+    ma, mr = assert_close(got, ref, *TOL[w.kv_dtype], what=f"{w.name} decode, all sequences")
+    print(f"[{w.name} decode, {w.num_seqs} sequences] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
+def test_full_size_store_decode_vs_oracle(full_size):
+    """pa_store_decode (newest tokens stored in the decode launch): every
+    sequence's output and the whole pools against the oracle."""
+    w, kc, vc, ref = full_size
+    case, k, v, slots = _fused_case(w)
+    got = bf16_f64(host_bits(_store_decode(case, k, v, slots)))
+    _check_pools_equal(case, kc, vc)
+    ma, mr = assert_close(got, ref, *TOL[w.kv_dtype], what=f"{w.name} store+decode, all sequences")
+    print(f"[{w.name} store+decode, {w.num_seqs} sequences] max_abs={ma:.3e} max_rel={mr:.3e}")
+
+
 @pytest.mark.parametrize("number", [3, 5], ids=["qwen3-8b", "fp8-long"])
 def test_store_decode_full_size_matches_two_launches(number):
-    """Qwen3-8B (shared prefix, split contexts) and fp8 long context: the fused
-    call gives the bits of pa_store_kv + pa_decode, output and pools."""
+    """The fused call gives the bits of pa_store_kv + pa_decode, output and pools."""
     w = W.make(number)
     print(w.name, flush=True)
     fused, k, v, slots = _fused_case(w)
@@ -173,48 +184,6 @@ def test_store_decode_full_size_matches_two_launches(number):
     want = host_bits(two.decode())
     assert np.array_equal(got, want)
     assert np.array_equal(fk, host_bits(two.k_cache)) and np.array_equal(fv, host_bits(two.v_cache))
-
-
-def test_qwen3_8b_shared_prefix_sampled():
-    w = W.make(3)
-    case = GpuCase(w)
-    lens = w.context_lens
-    sharers = np.flatnonzero((w.block_tables[:, :2] == w.shared_blocks).all(axis=1))
-    rng = np.random.default_rng(0)
-    seqs = sorted(set([int(lens.argmax()), int(lens.argmin())] + sharers[:6].tolist()
-                      + rng.choice(w.num_seqs, 16, replace=False).tolist()))
-    kc, vc, blocks = _oracle_pools_for(w, seqs)
-    got = bf16_f64(host_bits(case.decode()))
-    ref = _oracle_decode(w, kc, vc, seqs=seqs)
-    ma, mr = assert_close(got[seqs], ref[seqs], *TOL["bf16"], what="qwen3-8b sampled")
-    print(f"[qwen3-8b decode, {len(seqs)} sampled] max_abs={ma:.3e} max_rel={mr:.3e}")
-    # the sampled sequences' blocks hold exactly the oracle's bytes at valid positions
-    for s in seqs[:4]:
-        n = int(lens[s])
-        Kg, Vg = oracle.cache.depage_raw(host_bits(case.k_cache[torch.as_tensor(blocks).cuda()]),
-                                         host_bits(case.v_cache[torch.as_tensor(blocks).cuda()]),
-                                         np.searchsorted(blocks, w.block_tables[s]), n, w.block_size)
-        Ko, Vo = oracle.cache.depage_raw(kc, vc, w.block_tables[s], n, w.block_size)
-        assert np.array_equal(Kg, Ko) and np.array_equal(Vg, Vo)
-
-
-def test_fp8_long_context_sampled():
-    w = W.make(5)
-    case = GpuCase(w)
-    lens = w.context_lens
-    seqs = sorted({int(lens.argmax()), int(lens.argmin()), 0, 1, 17, 40})
-    kc, vc, blocks = _oracle_pools_for(w, seqs)
-    got = bf16_f64(host_bits(case.decode()))
-    ref = _oracle_decode(w, kc, vc, seqs=seqs)
-    ma, mr = assert_close(got[seqs], ref[seqs], *TOL["fp8"], what="fp8 long sampled")
-    print(f"[fp8 long decode, {len(seqs)} sampled] max_abs={ma:.3e} max_rel={mr:.3e}")
-    for s in seqs[:3]:
-        n = int(lens[s])
-        idx = torch.as_tensor(blocks).cuda()
-        Kg, Vg = oracle.cache.depage_raw(host_bits(case.k_cache[idx]), host_bits(case.v_cache[idx]),
-                                         np.searchsorted(blocks, w.block_tables[s]), n, w.block_size)
-        Ko, Vo = oracle.cache.depage_raw(kc, vc, w.block_tables[s], n, w.block_size)
-        assert np.array_equal(Kg, Ko) and np.array_equal(Vg, Vo)
 
 
 # ---------------------------------------------------------------- invariants and closed forms

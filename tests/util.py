@@ -91,3 +91,26 @@ def relabel_blocks(w, seed=0):
     w2.poison_block = int(pi[w.poison_block])
     w2.unused_blocks = np.sort(pi[w.unused_blocks]).astype(np.int32)
     return w2
+
+
+def oracle_decode_threads(w, kc, vc, seqs=None):
+    """oracle.attention.decode of the given sequences (default: all), the
+    sequences split over host threads; each call fills only its own rows, so
+    the sum of the partial results is the oracle's result."""
+    import concurrent.futures
+    import os
+
+    import oracle
+    seqs = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
+    # longest sequences first, dealt round-robin so the threads get equal work
+    order = sorted(seqs, key=lambda s: -int(w.context_lens[s]))
+    parts = [order[i::workers] for i in range(workers)]
+
+    def run(part):
+        return oracle.attention.decode(w.q, kc, vc, w.block_tables, w.context_lens, w.scale,
+                                       w.block_size, w.k_scale, w.v_scale, seqs=part)
+
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        outs = list(ex.map(run, [p for p in parts if p]))
+    return np.sum(outs, axis=0)
