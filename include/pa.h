@@ -175,24 +175,32 @@ pa_status pa_store_decode(const void* q, const void* new_k, const void* new_v,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* pa_prefill_varlen — causal attention of packed query chunks over their
- * sequences' paged keys (cached prefix plus the chunk itself, already written by
- * pa_store_kv): chunked prefill ("nano-vllm-lite…", 核心技术改进 §2).
+ * sequences' keys (cached prefix plus the chunk itself): chunked prefill
+ * ("nano-vllm-lite…", 核心技术改进 §2). Two sources of keys/values:
+ *  - paged (block_tables != NULL): k_cache, v_cache are the pools, bf16 or fp8,
+ *    already holding the chunk's tokens (written by pa_store_kv). An fp8 pool is
+ *    read through cache->k_scale / v_scale exactly as pa_decode reads it: each
+ *    E4M3 byte widened to bf16 without rounding, k_scale[h] folded into the
+ *    softmax scale, v_scale[h] into the output;
+ *  - packed (block_tables == NULL): k_cache, v_cache are device bf16
+ *    [total_k][num_kv_heads][head_dim], sequence s owning rows
+ *    cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1 (a contiguous KV buffer, no pool).
+ *    Only cache->num_kv_heads, head_dim and dtype are read; dtype must be
+ *    PA_KV_BF16 (else PA_ERR_UNSUPPORTED); max_blocks_per_seq is ignored.
  *   q             device bf16 [total_q][num_q_heads][head_dim]; sequence s owns
  *                 rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1
- *   k_cache, v_cache  the paged pools, bf16 or fp8 (an fp8 pool is read through
- *                 cache->k_scale / v_scale exactly as pa_decode reads it: each
- *                 E4M3 byte widened to bf16 without rounding, k_scale[h] folded
- *                 into the softmax scale, v_scale[h] into the output)
  *   cu_seqlens_q, cu_seqlens_k  device int32 [num_seqs+1] prefix sums; sequence s
  *                 has Lq = cu_q[s+1]-cu_q[s] queries and Lk = cu_k[s+1]-cu_k[s]
- *                 keys at logical positions 0..Lk-1 of its block table
- *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *                 keys (logical positions 0..Lk-1 of its block table when paged)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq], or NULL (packed)
  *   max_seqlen_q, max_seqlen_k  host bounds >= every Lq, Lk; Lq is clamped to
- *                 max_seqlen_q and Lk to min(max_seqlen_k, max_blocks_per_seq*block_size)
+ *                 max_seqlen_q and Lk to max_seqlen_k (paged: also to
+ *                 max_blocks_per_seq*block_size)
  *   scale         softmax scale, finite and > 0 (else PA_ERR_SHAPE)
  *   out           device bf16 [total_q][num_q_heads][head_dim]
  * Query i of sequence s sits at position Lk-Lq+i and attends to keys 0..Lk-Lq+i
- * (mask aligned bottom-right); a row that sees no key is written as zeros. */
+ * (mask aligned bottom-right); a row that sees no key is written as zeros.
+ * Packed keys are read only at rows below cu_seqlens_k[s+1]. */
 pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,

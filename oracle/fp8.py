@@ -72,7 +72,8 @@ def quantize_bf16(bits, scale_f32) -> np.ndarray:
     table = _QUANT_TABLES.get(key)
     if table is None:
         every = (np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)).view(np.float32)
-        table = _QUANT_TABLES[key] = quantize(every, np.float32(scale_f32))
+        with np.errstate(over="ignore", invalid="ignore"):   # inf / NaN patterns: saturate / NaN code
+            table = _QUANT_TABLES[key] = quantize(every, np.float32(scale_f32))
     return table[np.asarray(bits, dtype=np.uint16)]
 
 

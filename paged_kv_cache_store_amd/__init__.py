@@ -257,26 +257,41 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
 
 def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, scale,
                    max_seqlen_q, max_seqlen_k, out=None, k_scale=None, v_scale=None, stream=None):
-    """Causal varlen prefill over the paged pools; returns out ([Tq, Hq, D] bf16).
-    fp8 pools need k_scale / v_scale (device float32 [num_kv_heads])."""
-    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
-    dev = k_cache.device
+    """Causal varlen prefill; returns out ([Tq, Hq, D] bf16).
+    Paged: k_cache / v_cache are the pools and block_tables [S, MB] int32 (fp8
+    pools need k_scale / v_scale, device float32 [num_kv_heads]).
+    Packed: block_tables=None and k_cache / v_cache are bf16 [Tk, Hkv, D], the
+    keys of sequence s in rows cu_seqlens_k[s] .. cu_seqlens_k[s+1]-1."""
+    dev = q.device
     _check(q, "q", torch.bfloat16, 3, dev)
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, dev)
     _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, dev)
-    _check(block_tables, "block_tables", torch.int32, 2, dev)
     S = cu_seqlens_q.numel() - 1
-    if cu_seqlens_k.numel() != S + 1 or block_tables.shape[0] != S or q.shape[2] != d:
-        raise ValueError("cu_seqlens_q/k [S+1], block_tables [S, MB] and q [Tq, Hq, D] disagree")
+    if block_tables is None:
+        _check(k_cache, "k", torch.bfloat16, 3, dev)
+        _check(v_cache, "v", torch.bfloat16, 3, dev)
+        tk, hkv, d = k_cache.shape
+        if tuple(v_cache.shape) != (tk, hkv, d):
+            raise ValueError("packed k and v must both be [Tk, Hkv, D]")
+        desc = CacheDesc(0, 0, hkv, d, PA_KV_BF16, None, None)
+        mb, table = 0, None
+    else:
+        desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
+        _check(block_tables, "block_tables", torch.int32, 2, dev)
+        if block_tables.shape[0] != S:
+            raise ValueError("block_tables must be [S, MB] with S = len(cu_seqlens_q) - 1")
+        mb, table = block_tables.shape[1], block_tables
+    if cu_seqlens_k.numel() != S + 1 or q.shape[2] != d:
+        raise ValueError("cu_seqlens_q/k [S+1] and q [Tq, Hq, D] disagree")
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", torch.bfloat16, 3, dev)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
     st = library().pa_prefill_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens_q),
-                                _ptr(cu_seqlens_k), _ptr(block_tables), block_tables.shape[1], S,
-                                q.shape[1], int(max_seqlen_q), int(max_seqlen_k), float(scale),
-                                _ptr(out), ctypes.byref(desc), _stream(stream))
+                                     _ptr(cu_seqlens_k), _ptr(table), mb, S, q.shape[1], int(max_seqlen_q),
+                                     int(max_seqlen_k), float(scale), _ptr(out), ctypes.byref(desc),
+                                     _stream(stream))
     if st != 0:
         raise PaError(st, "pa_prefill_varlen")
     return out

@@ -9,6 +9,7 @@ paged_kv_cache_store_amd/libpa.so next to this file. Flags:
 * IEEE-correct float32 division kept explicit
   (-fhip-fp32-correctly-rounded-divide-sqrt): the fp8 store depends on it.
 """
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -46,15 +47,19 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     """Compile every source and link libpa.so (or `out`); returns the library path.
     `defines` are extra -D macros (tuning variants of the kernels)."""
     with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
-        objs = []
+        objs, cmds = [], []
         for src in SOURCES:
             obj = os.path.join(tmp, src.rsplit(".", 1)[0] + ".o")
             cmd = [HIPCC, *DEVICE_FLAGS, *["-D" + d for d in defines], "-I", INCLUDE, "-I", CSRC, "-c",
                    os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd))
-            _run(cmd)
+            cmds.append(cmd)
             objs.append(obj)
+        # one compiler process per source, at most as many as usable cores
+        workers = max(1, min(len(cmds), len(os.sched_getaffinity(0)), 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(_run, cmds))
         out_tmp = os.path.join(tmp, "libpa.so")
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp])
         shutil.move(out_tmp, out)

@@ -206,27 +206,45 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                             int32_t max_seqlen_k, float scale, void* out,
                             const pa_cache_desc* cache, hipStream_t stream) {
   pa::PoolDims dims;
-  pa_status st = check_cache(cache, &dims);
-  if (st != PA_OK) return st;
+  const bool packed = block_tables == nullptr;
+  if (packed) {
+    // packed keys/values: only the head counts, head_dim and dtype of the
+    // descriptor are read
+    if (!cache) return PA_ERR_NULL;
+    if (cache->num_kv_heads <= 0 || cache->head_dim <= 0) return PA_ERR_SHAPE;
+    if (cache->head_dim != 64 && cache->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (cache->dtype != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
+    dims.num_blocks = 0;
+    dims.block_size = 0;
+    dims.num_kv_heads = cache->num_kv_heads;
+    dims.head_dim = cache->head_dim;
+    dims.fp8 = false;
+  } else {
+    pa_status st = check_cache(cache, &dims);
+    if (st != PA_OK) return st;
+  }
   if (num_seqs < 0 || num_q_heads <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
-      max_blocks_per_seq <= 0)
+      (!packed && max_blocks_per_seq <= 0))
     return PA_ERR_SHAPE;
   if (num_q_heads % dims.num_kv_heads != 0) return PA_ERR_SHAPE;
   if (!supported_group(num_q_heads / dims.num_kv_heads)) return PA_ERR_UNSUPPORTED;
   if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_SHAPE;
   if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
-    return PA_ERR_NULL;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !out) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(block_tables, 4))
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || (!packed && !aligned(block_tables, 4)))
     return PA_ERR_UNSUPPORTED;
-  const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
-  const int32_t cap_k = int32_t(cap_ll < max_seqlen_k ? cap_ll : max_seqlen_k);
+  int32_t cap_k = max_seqlen_k;
+  if (!packed) {
+    const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
+    cap_k = int32_t(cap_ll < max_seqlen_k ? cap_ll : max_seqlen_k);
+  }
   return hip_status(pa::launch_prefill(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
                                        static_cast<const uint8_t*>(v_cache), cu_seqlens_q, cu_seqlens_k,
-                                       block_tables, max_blocks_per_seq, num_seqs, num_q_heads,
+                                       block_tables, packed ? 0 : max_blocks_per_seq, num_seqs, num_q_heads,
                                        max_seqlen_q, cap_k, scale, static_cast<uint16_t*>(out), dims,
-                                       cache->k_scale, cache->v_scale, stream));
+                                       packed ? nullptr : cache->k_scale, packed ? nullptr : cache->v_scale,
+                                       stream));
 }
 
 pa_status pa_add_rmsnorm(const void* x, const void* residual, const void* weight, int32_t num_tokens,

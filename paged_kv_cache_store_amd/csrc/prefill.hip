@@ -24,6 +24,10 @@
 //   {4h..4h+3, 8+4h..8+4h+3} of each 16-key step; one v_permlane32_swap per
 //   dword pair regroups them to keys 8h..8h+7, one 8-key V chunk, so every A
 //   fragment is one 16-byte read.
+// * packed keys/values (no block table: K and V are [Tk][Hkv][D] bf16, each
+//   sequence's keys contiguous from row cu_k[s]) take the register path: K
+//   chunks are copied as they are, V is transposed 8 keys x 8 head-dims at a
+//   time into the same LDS layouts, so the MFMA loop is unchanged.
 #include <math.h>
 
 #include "pa_device.h"
@@ -112,7 +116,7 @@ static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
 // (query row, head) columns, i.e. 128 * kNB / G query rows of each of the G heads.
-template <int kD, int kG, int kNB, bool kFp8, bool kBig>
+template <int kD, int kG, int kNB, bool kFp8, bool kBig, bool kPacked = false>
 __global__ __launch_bounds__(kPrefillThreads)
 #if PA_PREFILL_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
@@ -127,7 +131,8 @@ void prefill_kernel(const PrefillArgs a) {
   constexpr int kKLoads = (kD / kX) * kBN / kPrefillThreads;   // 16-byte K loads per thread per tile
   constexpr int kVLoads = (kBN / kX) * kD / kPrefillThreads;
 
-  constexpr bool kDirect = !kFp8;        // bf16 tiles go from the pool straight into LDS
+  static_assert(!(kPacked && (kFp8 || kBig)), "packed keys/values are bf16, without blocks");
+  constexpr bool kDirect = !kFp8 && !kPacked;   // bf16 pool tiles go straight into LDS
   constexpr int kKW = kKC / kPrefillWaves;                   // direct: K chunk rows per wave
   constexpr int kVW = (kBN / 8) * (kD / 64) / kPrefillWaves; // direct: 64-wide V rows per wave
 
@@ -186,7 +191,7 @@ void prefill_kernel(const PrefillArgs a) {
   const int row0 = qb * kBM;
   if (row0 >= Lq || Lq <= 0) return;
   const int bs = a.block_size;
-  const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq;
+  const int* bt = kPacked ? nullptr : a.block_tables + (long long)s * a.max_blocks_per_seq;
   const long long slab16 = (long long)bs * kD * (kFp8 ? 1 : 2) / 16;
   const uint4* kpool = reinterpret_cast<const uint4*>(a.k_cache) + (long long)hk * slab16;
   const uint4* vpool = reinterpret_cast<const uint4*>(a.v_cache) + (long long)hk * slab16;
@@ -245,12 +250,14 @@ void prefill_kernel(const PrefillArgs a) {
   int wbase = 0;
   auto load_ids = [&](int first) {   // every thread calls it; the caller synchronises
     wbase = first;
-    for (int i = tid; i < kIdCache && first + i < nblk; i += kPrefillThreads) ids_s[i] = bt[first + i];
+    if constexpr (!kPacked)
+      for (int i = tid; i < kIdCache && first + i < nblk; i += kPrefillThreads) ids_s[i] = bt[first + i];
   };
   auto block_of = [&](int key) { return ids_s[(key >> bshift) - wbase]; };
   // move the window so that it holds every block tiles t0..t1 read (uniform
   // branch; two tiles span at most 8 blocks, far fewer than the window)
   auto ensure_ids = [&](int t0, int t1) {
+    if constexpr (kPacked) return;
     const int lastk = (t1 * kBN + kBN < Lk ? t1 * kBN + kBN : Lk) - 1;
     if ((lastk >> bshift) - wbase >= kIdCache) {
       __syncthreads();
@@ -264,7 +271,18 @@ void prefill_kernel(const PrefillArgs a) {
   const int v_j0 = tid / kD;              // staged V: first 16-key chunk
   // staging registers use a native vector type: with HIP's union-based uint4 the
   // array is not split into registers and the backend moves it into LDS
-  u32x4_t kreg[kDirect ? 1 : kKLoads], vreg[kDirect ? 1 : kVLoads];
+  constexpr int kVRegs = kDirect ? 1 : (kPacked ? 8 : kVLoads);
+  u32x4_t kreg[kDirect ? 1 : kKLoads], vreg[kVRegs];
+  // packed: row cu_k[s] of K / V for this KV head, rows Hkv*D elements apart
+  const long long prow = (long long)Hkv * kD;
+  const uint16_t* kseq = kPacked ? reinterpret_cast<const uint16_t*>(a.k_cache) +
+                                       ((long long)a.cu_k[s] * Hkv + hk) * kD : nullptr;
+  const uint16_t* vseq = kPacked ? reinterpret_cast<const uint16_t*>(a.v_cache) +
+                                       ((long long)a.cu_k[s] * Hkv + hk) * kD : nullptr;
+  // packed V: thread tid < kVItems transposes 8 keys (8-key chunk pv_j) x 8 head-dims (pv_g)
+  constexpr int kVItems = (kBN / 8) * (kD / 8);
+  const int pv_j = tid / (kD / 8);
+  const int pv_g = tid % (kD / 8);
   // direct: the V row filled by load u of this wave: 8-key chunk j, head-dims 64*dh ..
   auto vrow = [&](int u, int& j, int& dh) {
     const int e = w * kVW + u;
@@ -341,7 +359,21 @@ void prefill_kernel(const PrefillArgs a) {
   // staged (fp8): loads into registers ...
   auto load_tile = [&](int kt) {
     const int key0 = kt * kBN;
-    if constexpr (kBig) {
+    if constexpr (kPacked) {
+      // keys past Lk read key Lk-1 (K: scores masked) or nothing (V: zeros)
+      const int key = key0 + k_key < Lk ? key0 + k_key : Lk - 1;
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u)
+        kreg[u] = *reinterpret_cast<const u32x4_t*>(kseq + key * prow + (k_c0 + u * (kPrefillThreads / kBN)) * 8);
+      if (tid < kVItems) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int vkey = key0 + pv_j * 8 + e;
+          vreg[e] = vkey < Lk ? *reinterpret_cast<const u32x4_t*>(vseq + vkey * prow + pv_g * 8)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    } else if constexpr (kBig) {
       const int blk = __builtin_amdgcn_readfirstlane(block_of(key0));
       const u32x4_t* kb = reinterpret_cast<const u32x4_t*>(kpool + (long long)blk * blk16 + (key0 & bmask));
 #pragma unroll
@@ -372,6 +404,29 @@ void prefill_kernel(const PrefillArgs a) {
   // ... widened to bf16 and written to LDS (every e4m3 value is a bf16 value);
   // V values past Lk are zeroed on the bytes first
   auto store_tile = [&](uint4 (*ks)[kBN], uint4 (*vs)[kD], int kt) {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u) {
+        const int c = k_c0 + u * (kPrefillThreads / kBN);
+        ks[c][k_key] = make_uint4(kreg[u][0], kreg[u][1], kreg[u][2], kreg[u][3]);
+      }
+      if (tid < kVItems) {
+        // vreg[e] holds head-dims 8*pv_g .. +7 of key 8*pv_j + e; entry
+        // vs[pv_j][d] takes keys 8*pv_j .. +7 of head-dim d, two per dword
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (vreg[2 * i][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+            const uint32_t hi = (vreg[2 * i + 1][dd / 2] >> (16 * (dd % 2))) & 0xffffu;
+            wv[i] = lo | (hi << 16);
+          }
+          vs[pv_j][pv_g * 8 + dd] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u) {
       const int c8 = k_c0 + u * (kPrefillThreads / kBN);   // head-dims 16*c8 .. 16*c8+15
@@ -683,19 +738,20 @@ void prefill_kernel(const PrefillArgs a) {
 
 constexpr int kNBLaunch = PA_PREFILL_NB;
 
-template <int kD, bool kFp8, bool kBig>
+template <int kD, bool kFp8, bool kBig, bool kPacked = false>
 static bool launch_prefill_gb(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
   switch (G) {
-    case 1: prefill_kernel<kD, 1, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 2: prefill_kernel<kD, 2, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 4: prefill_kernel<kD, 4, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
-    case 8: prefill_kernel<kD, 8, kNBLaunch, kFp8, kBig><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 1: prefill_kernel<kD, 1, kNBLaunch, kFp8, kBig, kPacked><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 2: prefill_kernel<kD, 2, kNBLaunch, kFp8, kBig, kPacked><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 4: prefill_kernel<kD, 4, kNBLaunch, kFp8, kBig, kPacked><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
+    case 8: prefill_kernel<kD, 8, kNBLaunch, kFp8, kBig, kPacked><<<grid, kPrefillThreads, 0, stream>>>(a); return true;
     default: return false;
   }
 }
 
 template <int kD, bool kFp8>
 static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStream_t stream) {
+  if (!a.block_tables) return !kFp8 && launch_prefill_gb<kD, false, false, true>(G, a, grid, stream);
   return a.block_size >= kBN ? launch_prefill_gb<kD, kFp8, true>(G, a, grid, stream)
                              : launch_prefill_gb<kD, kFp8, false>(G, a, grid, stream);
 }
@@ -723,7 +779,7 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool.num_kv_heads;
   a.block_size = pool.block_size;
-  a.block_shift = __builtin_ctz(unsigned(pool.block_size));
+  a.block_shift = block_tables ? __builtin_ctz(unsigned(pool.block_size)) : 0;
   a.max_seqlen_q = max_seqlen_q;
   a.cap_k = max_seqlen_k;
   a.num_qblocks = (max_seqlen_q + bm - 1) / bm;

@@ -109,8 +109,8 @@ def test_workspace_and_partition_rules(lib):
     assert lib.pa_decode_workspace_size(64, 32, 128, 32768, 0) == 64 * 32 * (32768 // P) * 130 * 4
 
 
-def prefill(lib, d, q=FAKE, S=2, hq=4, mq=16, mk=64, mb=8, scale=0.125):
-    return lib.pa_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, FAKE, mb, S, hq, mq, mk, scale, FAKE,
+def prefill(lib, d, q=FAKE, S=2, hq=4, mq=16, mk=64, mb=8, scale=0.125, bt=FAKE):
+    return lib.pa_prefill_varlen(q, FAKE, FAKE, FAKE, FAKE, bt, mb, S, hq, mq, mk, scale, FAKE,
                                  ctypes.byref(d) if d is not None else None, None)
 
 
@@ -124,6 +124,25 @@ def test_prefill_validation(lib):
     assert prefill(lib, desc(), S=0, q=None) == OK
     for bad in (0.0, -0.5, float("inf"), float("nan")):
         assert prefill(lib, desc(), scale=bad) == SHAPE
+
+
+def test_prefill_packed_validation(lib):
+    """No block table: packed bf16 keys/values; only head counts, head_dim and
+    dtype of the descriptor matter (no pool, no max_blocks_per_seq)."""
+    assert prefill(lib, None, bt=None) == NULL
+    assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE), bt=None) == UNSUP   # packed is bf16 only
+    nopool = desc()
+    nopool.num_blocks, nopool.block_size = 0, 0
+    assert prefill(lib, nopool, bt=None, S=0, q=None) == OK
+    assert prefill(lib, nopool, bt=None, mb=0, S=0, q=None) == OK
+    assert prefill(lib, nopool, bt=None, hq=5) == SHAPE
+    assert prefill(lib, nopool, bt=None, q=None) == NULL
+    assert prefill(lib, nopool, bt=None, q=ctypes.c_void_p(0x1008)) == UNSUP
+    d64 = desc()
+    d64.head_dim = 96
+    assert prefill(lib, d64, bt=None) == UNSUP
+    # with a table, the pool must be a valid one
+    assert prefill(lib, nopool) == SHAPE
 
 
 def norm(lib, x=FAKE, r=FAKE, w=FAKE, T=4, H=64, eps=1e-6, out=ctypes.c_void_p(0x2000),

@@ -243,3 +243,85 @@ def test_prefill_guard_bands_and_determinism():
     assert np.array_equal(first, host_bits(buf))
     sentinel = host_bits(torch.full((Hq, D), -7.0, dtype=torch.bfloat16))
     assert np.array_equal(first[0], sentinel) and np.array_equal(first[Tq + 1], sentinel)
+
+
+# ---------------------------------------------------------------- packed keys/values (no block table)
+PACKED = [
+    dict(seed=340, Hq=4, Hkv=1, D=128, bs=16, prefill=[(0, 1), (0, 17), (0, 64), (0, 65), (16, 16)]),
+    dict(seed=341, Hq=8, Hkv=2, D=128, bs=64, prefill=[(100, 30), (37, 200), (0, 300), (256, 64)]),
+    dict(seed=342, Hq=32, Hkv=8, D=128, bs=256, prefill=[(0, 512), (768, 512), (1000, 77)]),
+    dict(seed=343, Hq=16, Hkv=8, D=64, bs=32, prefill=[(5, 250), (0, 129), (300, 1)]),
+    dict(seed=344, Hq=8, Hkv=1, D=64, bs=128, prefill=[(0, 40), (200, 33), (64, 70)]),
+]
+
+
+def _packed_kv(w):
+    """Each sequence's Lk keys/values in logical order, sequences one after the
+    other ([Tk, Hkv, D] bf16 bits), taken from the generator's token lists."""
+    from tests.util import logical_kv, slot_index
+    idx = slot_index(w)
+    ks, vs = [], []
+    for s in range(len(w.cu_seqlens_k) - 1):
+        lk = int(w.cu_seqlens_k[s + 1] - w.cu_seqlens_k[s])
+        K, V = logical_kv(w, w.p_block_tables[s], lk, idx)
+        ks.append(K)
+        vs.append(V)
+    return np.concatenate(ks), np.concatenate(vs)
+
+
+def _identity_pool(w, K, V):
+    """Oracle pool holding the packed keys with sequence s in consecutive blocks
+    from block first[s] (an identity block table per sequence)."""
+    bs = w.block_size
+    S = len(w.cu_seqlens_k) - 1
+    lens = np.diff(w.cu_seqlens_k)
+    nblk = -(-lens // bs)
+    first = np.concatenate([[0], np.cumsum(nblk)])
+    ks, vs = oracle.cache.pool_shapes(int(first[-1]) + 1, w.num_kv_heads, bs, w.head_dim)
+    kc = np.full(ks, W.BF16_NAN, np.uint16)
+    vc = np.full(vs, W.BF16_NAN, np.uint16)
+    slots = np.concatenate([first[s] * bs + np.arange(lens[s]) for s in range(S)]).astype(np.int32)
+    oracle.cache.store(K, V, slots, kc, vc, bs)
+    table = np.zeros((S, max(1, int(nblk.max()))), np.int32)
+    for s in range(S):
+        table[s, :nblk[s]] = first[s] + np.arange(nblk[s])
+    return kc, vc, table
+
+
+@pytest.mark.parametrize("cfg", PACKED, ids=[f"packed{i}" for i in range(len(PACKED))])
+def test_prefill_packed_kv(cfg):
+    """block_tables = NULL: keys/values packed [Tk, Hkv, D] by cu_seqlens_k.
+    Every row against the oracle (fed the same keys through an identity-table
+    pool), and bit-identical to the paged call over the same keys."""
+    import paged_kv_cache_store_amd as pa
+    print(f"case {cfg}", flush=True)
+    w = W.custom(context_lens=(), **cfg)
+    K, V = _packed_kv(w)
+    kd, vd = dev_bf16(K), dev_bf16(V)
+    q = dev_bf16(w.pq)
+    cu_q, cu_k = dev_i32(w.cu_seqlens_q), dev_i32(w.cu_seqlens_k)
+    got = pa.prefill_varlen(q, kd, vd, cu_q, cu_k, None, float(w.scale), w.max_seqlen_q, w.max_seqlen_k)
+    torch.cuda.synchronize()
+    kc, vc, table = _identity_pool(w, K, V)
+    ref = oracle.attention.prefill(w.pq, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, table, w.scale,
+                                   w.block_size)
+    ma, mr = assert_close(bf16_f64(host_bits(got)), ref, *TOL, what="packed prefill")
+    print(f"max_abs={ma:.3e} max_rel={mr:.3e}")
+    paged = GpuCase(w).prefill()
+    assert np.array_equal(host_bits(got), host_bits(paged))
+
+
+def test_prefill_packed_mixed_step_shapes():
+    """The mixed step's 8 chunks (512 new tokens on prefixes 0..1792, 32/8
+    heads, D 128) with packed keys/values: every row against the oracle."""
+    import paged_kv_cache_store_amd as pa
+    w = W.make(4)
+    K, V = _packed_kv(w)
+    got = pa.prefill_varlen(dev_bf16(w.pq), dev_bf16(K), dev_bf16(V), dev_i32(w.cu_seqlens_q),
+                            dev_i32(w.cu_seqlens_k), None, float(w.scale), w.max_seqlen_q, w.max_seqlen_k)
+    torch.cuda.synchronize()
+    kc, vc, table = _identity_pool(w, K, V)
+    ref = oracle.attention.prefill(w.pq, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, table, w.scale,
+                                   w.block_size)
+    ma, mr = assert_close(bf16_f64(host_bits(got)), ref, *TOL, what="packed mixed-step prefill")
+    print(f"[packed mixed prefill] max_abs={ma:.3e} max_rel={mr:.3e}")
