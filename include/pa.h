@@ -107,8 +107,11 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
                       int32_t num_tokens, void* k_cache, void* v_cache,
                       const pa_cache_desc* cache, hipStream_t stream);
 
-/* Bytes of device workspace pa_decode needs for these bounds (0 when no
- * sequence can span more than one partition). partition_size as in pa_decode. */
+/* Bytes of device workspace pa_decode needs for these bounds: the split-context
+ * partials when a context can span more than one partition, plus, for
+ * num_seqs >= 128, the order in which the sequences are processed (longest
+ * first, ranked on the device by a small kernel launched before the decode).
+ * 0 when neither applies. partition_size as in pa_decode. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
 
@@ -137,7 +140,10 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                 a 256-entry table: partition/block_size > 256 is
  *                 PA_ERR_UNSUPPORTED
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
- *                 (may be NULL when that size is 0); contents on entry ignored
+ *                 (may be NULL when that size is 0); contents on entry ignored.
+ *                 With num_seqs >= 128 an extra kernel ranks the sequences by
+ *                 context length into it first (longest first), so the launch
+ *                 does not end on a tail of long sequences
  * Query head h reads KV head h / (num_q_heads / num_kv_heads); the group size
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8. Output: softmax(scale*q.k)
  * weighted sum of v, float32 accumulation, rounded to nearest-even bf16. */
@@ -148,24 +154,27 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* pa_store_decode — pa_store_kv of each sequence's newest token followed by
- * pa_decode, in one launch (the store and the decode are the two halves of a
+/* pa_store_decode — a decode step: pa_store_kv of each sequence's newest token
+ * and pa_decode, in one call (the store and the decode are the two halves of a
  * decode step: "Nano-vLLM…", 三.1 and 三.3).
  *   new_k, new_v  device bf16 [num_seqs][num_kv_heads][head_dim]: sequence s's
  *                 newest token
  *   slot_mapping  device int32 [num_seqs]: its slot; < 0 or >= num_blocks*block_size
  *                 skips the write (as in pa_store_kv)
- *   k_cache, v_cache  written at those slots, and read
+ *   k_cache, v_cache  read by the decode, then written at those slots
  *   every other argument, the workspace rule and the status codes as in
  *   pa_decode; NULL new_k / new_v / slot_mapping with num_seqs > 0 -> PA_ERR_NULL.
- * Result: the pool bytes and the output of pa_store_kv(new_k, new_v,
- * slot_mapping) followed by pa_decode on the same stream, bit for bit, when
- * every written slot is either the slot of position context_lens[s]-1 of its
- * own sequence s (through block_tables) or a slot no sequence reads in this
- * call; otherwise the output is undefined (a block shared by several sequences
- * is copied before it is written into). In the first case the kernel takes the
- * token from registers for that position and writes the pool after its last
- * read; any other slot is written before the decode reads. */
+ * Two launches on `stream`: the decode, which takes position
+ * context_lens[s]-1 of sequence s from new_k / new_v (in the pool's
+ * representation: the bf16 bits, or the fp8 code pa_store_kv would store)
+ * when slot_mapping[s] is that position's slot, then the store of the tokens.
+ * The decode thus never reads pool lines the step has just written, which is
+ * faster than storing first. Result: the pool bytes and the output of
+ * pa_store_kv(new_k, new_v, slot_mapping) followed by pa_decode on the same
+ * stream, bit for bit, when every written slot is either the slot of position
+ * context_lens[s]-1 of its own sequence s (through block_tables) or a slot no
+ * sequence reads in this call; otherwise the output is undefined (a block
+ * shared by several sequences is copied before it is written into). */
 pa_status pa_store_decode(const void* q, const void* new_k, const void* new_v,
                           const int32_t* slot_mapping, void* k_cache, void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,

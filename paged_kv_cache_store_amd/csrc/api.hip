@@ -119,17 +119,19 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, max_context_len, partition_size);
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int32_t ctx = max_context_len < 0 ? 0 : max_context_len;
+  const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, ctx, partition_size);
   if (P <= 0) return 0;
-  const int32_t np = (max_context_len + P - 1) / P;
+  const int32_t np = ctx > 0 ? (ctx + P - 1) / P : 1;
   return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
 }
 
 namespace {
 
-// pa_decode and pa_store_decode: the same checks and launch; the second also
-// hands the newest tokens to the decode kernel, which stores them.
+// pa_decode and pa_store_decode: the same checks and decode launch; the second
+// hands the newest tokens to the decode kernel (which reads position n-1 from
+// them) and then launches their store.
 pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -162,16 +164,18 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const int32_t np = cap > 0 ? (cap + P - 1) / P : 1;
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, dims.head_dim, np);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-  return hip_status(pa::launch_decode(static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
-                                      static_cast<const uint8_t*>(v_cache), block_tables,
-                                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, cap,
-                                      scale, static_cast<uint16_t*>(out), dims, cache->k_scale,
-                                      cache->v_scale, P, workspace, stream,
-                                      fused ? static_cast<const uint16_t*>(new_k) : nullptr,
-                                      fused ? static_cast<const uint16_t*>(new_v) : nullptr,
-                                      fused ? slot_mapping : nullptr,
-                                      fused ? static_cast<uint8_t*>(const_cast<void*>(k_cache)) : nullptr,
-                                      fused ? static_cast<uint8_t*>(const_cast<void*>(v_cache)) : nullptr));
+  const hipError_t e = pa::launch_decode(
+      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
+      static_cast<const uint8_t*>(v_cache), block_tables, max_blocks_per_seq, context_lens, num_seqs,
+      num_q_heads, cap, scale, static_cast<uint16_t*>(out), dims, cache->k_scale, cache->v_scale, P,
+      workspace, stream, fused ? static_cast<const uint16_t*>(new_k) : nullptr,
+      fused ? static_cast<const uint16_t*>(new_v) : nullptr, fused ? slot_mapping : nullptr);
+  if (e != hipSuccess || !fused) return hip_status(e);
+  // the store of the newest tokens, after the decode that took them from new_k / new_v
+  return hip_status(pa::launch_store_kv(static_cast<const uint16_t*>(new_k), static_cast<const uint16_t*>(new_v),
+                                        slot_mapping, num_seqs, static_cast<uint8_t*>(const_cast<void*>(k_cache)),
+                                        static_cast<uint8_t*>(const_cast<void*>(v_cache)), dims,
+                                        cache->k_scale, cache->v_scale, stream));
 }
 
 }  // namespace

@@ -40,6 +40,11 @@ namespace pa {
 #define PA_DECODE_WAVES_PER_EU 0
 #endif
 
+// Sequences are taken longest first when there are at least this many (0: never)
+#ifndef PA_DECODE_ORDER_MIN_SEQS
+#define PA_DECODE_ORDER_MIN_SEQS 128
+#endif
+
 constexpr int kDecodeThreads = PA_DECODE_WAVES * 64;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
 constexpr int kTile = 64;            // keys per wave per step
@@ -57,6 +62,7 @@ struct DecodeArgs {
   float* part_o;
   float* part_m;
   float* part_l;
+  const int32_t* order;    // [num_seqs] sequences longest first, or nullptr (index order)
   int max_blocks_per_seq;
   int num_q_heads;
   int num_kv_heads;
@@ -65,19 +71,15 @@ struct DecodeArgs {
   int num_parts;   // NP = ceil(context cap / P)
   int ctx_cap;     // min(max_context_len, max_blocks_per_seq * block_size)
   float scale_log2;
-  // store fused into the decode (nullptr: none): the newest token of sequence s
+  // the newest token of each sequence from the caller (nullptr: none, read the pool)
   const uint16_t* new_k;   // [num_seqs][num_kv_heads][D]
   const uint16_t* new_v;
-  const int32_t* new_slots;  // [num_seqs]
-  uint8_t* k_store;        // the pools again, writable
-  uint8_t* v_store;
+  const int32_t* new_slots;  // [num_seqs]: its slot (the store launched after writes it there)
   long long num_slots;
 };
 
-// Inputs that no kernel of this file writes, read through the constant address
-// space: their uniform loads stay scalar loads even in the kernel that also
-// stores into the pools (the fused store), which the compiler cannot prove
-// disjoint from them.
+// Inputs that no kernel writes while the decode runs, read through the constant
+// address space, so that their uniform loads stay scalar loads.
 template <typename T>
 using const_as_ptr = const __attribute__((address_space(4))) T*;
 
@@ -86,14 +88,19 @@ __device__ __forceinline__ const_as_ptr<T> as_constant(const T* p) {
   return (const_as_ptr<T>)p;
 }
 
-// Fused store of the newest token of sequence s, KV head h. The token is kept
-// in LDS in the pool's representation (bf16 bits, or fp8 codes: the nearest
-// E4M3 code of the correctly rounded quotient value / scale, as the store
-// kernel writes them): bytes [0, D·es) hold K, [D·es, 2·D·es) hold V, value
-// order. The wave that reads the newest position takes it from there instead
-// of from the pool, and writes the pool only after its last load: a load of a
-// line this kernel has just partly written is served slowly, so the written
-// lines are never read back within the launch.
+// The newest token of sequence s, KV head h, taken from the caller's buffer
+// (pa_store_decode) instead of the pool. The store of these tokens runs as
+// its own launch after the decode, so the decode never reads a pool line the
+// step has just written: reading lines written by the store launch right
+// before was measured to slow the decode by 6-8 % (Qwen3-8B layer: 628 ->
+// 688 us), while the same writes into blocks nobody reads cost nothing, and
+// neither does the store launched after the decode (648 us for both).
+// The token is kept in LDS in the pool's representation (bf16 bits, or fp8
+// codes: the nearest E4M3 code of the correctly rounded quotient value /
+// scale, as the store kernel writes them): bytes [0, D·es) hold K,
+// [D·es, 2·D·es) hold V, value order. The wave that reads the newest position
+// puts it into that tile's registers, so the result is the one the pool will
+// hold once the store has run.
 
 // Lanes 0..D/4-1 each load 8 bf16 values (lanes below D/8: K, the rest: V).
 template <int kD>
@@ -124,44 +131,20 @@ __device__ __forceinline__ void stage_new_token(const DecodeArgs& a, uint4 x, in
   }
 }
 
-// Writes the staged token at its slot: lane c < D/x writes K chunk c (16 bytes),
-// lane l writes V values l and l + 64.
-template <int kD, bool kFp8>
-__device__ __forceinline__ void write_new_token(const DecodeArgs& a, long long slot, int h, int lane,
-                                                const uint8_t* tok_s) {
-  constexpr int kX = kFp8 ? 16 : 8;
-  constexpr int kEs = kFp8 ? 1 : 2;
-  const int bs = a.block_size;
-  const long long b = slot / bs;
-  const int o = int(slot % bs);
-  const long long slab = (b * a.num_kv_heads + h) * (long long)bs * kD;   // elements
-  if (lane < kD / kX) {
-    const long long k_el = slab + ((long long)lane * bs + o) * kX;
-    *reinterpret_cast<uint4*>(a.k_store + k_el * kEs) = reinterpret_cast<const uint4*>(tok_s)[lane];
-  }
-  const long long v_el = slab + (long long)(o / kX) * kD * kX + (o % kX);
-#pragma unroll
-  for (int i = 0; i < kD / kWave; ++i) {
-    const int d = lane + i * kWave;
-    const long long el = v_el + (long long)d * kX;
-    if constexpr (!kFp8)
-      reinterpret_cast<uint16_t*>(a.v_store)[el] = reinterpret_cast<const uint16_t*>(tok_s + kD * kEs)[d];
-    else
-      a.v_store[el] = tok_s[kD + d];
-  }
-}
-
-// Waves per SIMD the compiler must leave room for. Some fused-store variants
-// need a few more registers than the plain ones and would drop to 2 waves;
-// held at 3 they do not spill (fp8 with one query head per KV head would).
-constexpr int decode_min_waves(int g, bool fp8, bool store) {
+// Waves per SIMD the compiler must leave room for. The variants that take the
+// newest token from the caller need a few more registers than the plain ones
+// and would drop to 2 waves; held at 3 they do not spill (fp8 with one query
+// head per KV head would).
+constexpr int decode_min_waves(int g, bool fp8, bool with_new) {
   return PA_DECODE_WAVES_PER_EU ? PA_DECODE_WAVES_PER_EU
-                                : (store && g < 8 && !(fp8 && g == 1) ? 3 : 1);
+                                : (with_new && g < 8 && !(fp8 && g == 1) ? 3 : 1);
 }
 
-template <int kD, int kG, bool kFp8, bool kStore>
+// kNew: sequence s's position context_lens[s]-1 is read from new_k / new_v
+// (when new_slots[s] is that position's slot) instead of from the pool.
+template <int kD, int kG, bool kFp8, bool kNew>
 __global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(decode_min_waves(kG, kFp8, kStore))))
+__attribute__((amdgpu_waves_per_eu(decode_min_waves(kG, kFp8, kNew))))
 void decode_kernel(const DecodeArgs a) {
   constexpr int kX = kFp8 ? 16 : 8;       // elements per 16-byte chunk
   constexpr int kKC = kD / kX;            // K chunks per key
@@ -181,7 +164,7 @@ void decode_kernel(const DecodeArgs a) {
   const int h = bid % Hkv;  // KV head varies fastest: consecutive workgroups go to different XCDs
   const int rest = bid / Hkv;
   const int part = rest % a.num_parts;
-  const int s = rest / a.num_parts;
+  const int s = a.order ? as_constant(a.order)[rest / a.num_parts] : rest / a.num_parts;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave index, uniform
   const int lane = tid % kWave;
@@ -191,25 +174,20 @@ void decode_kernel(const DecodeArgs a) {
   int n = as_constant(a.context_lens)[s];   // scalar load: the tile loop's bounds stay uniform
   n = n < a.ctx_cap ? n : a.ctx_cap;
   const int p0 = part * P;
-  // Fused store: the newest token (position n-1) is handled by the one wave
-  // that reads that position, the wave given the partition's tile holding
-  // n-1 (wave 0 of partition 0 for an empty sequence).
-  __shared__ __attribute__((aligned(16))) uint8_t tok_s[kStore ? 2 * kD * (kFp8 ? 1 : 2) : 16];
+  // kNew: the newest token (position n-1) is loaded by the one wave that reads
+  // that position, the wave given the partition's tile holding n-1.
+  __shared__ __attribute__((aligned(16))) uint8_t tok_s[kNew ? 2 * kD * (kFp8 ? 1 : 2) : 16];
   const int t_new = n > 0 ? (n - 1 - p0) / kTile : -1;   // this partition's tile holding n-1
   long long slot_new = -1;
   uint4 tok = make_uint4(0, 0, 0, 0);
-  if constexpr (kStore) {
-    if (part == (n > 0 ? (n - 1) / P : 0) && (n <= 0 ? w == 0 : t_new % kDecodeWaves == w)) {
+  if constexpr (kNew) {
+    if (n > 0 && part == (n - 1) / P && t_new % kDecodeWaves == w) {
       slot_new = as_constant(a.new_slots)[s];
       if (slot_new >= a.num_slots) slot_new = -1;
     }
     if (slot_new >= 0) tok = load_new_token<kD>(a, s, h, lane);
   }
   if (n <= 0) {
-    if (kStore && slot_new >= 0) {
-      stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
-      write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
-    }
     if (part == 0) {
       for (int i = tid; i < kG * kD; i += kDecodeThreads)
         a.out[((long long)s * a.num_q_heads + h * kG) * kD + i] = 0;
@@ -224,7 +202,7 @@ void decode_kernel(const DecodeArgs a) {
   const int nb = (pend - p0 + bs - 1) / bs;
   const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq + p0 / bs;
   for (int i = tid; i < nb; i += kDecodeThreads) blk_s[i] = bt[i];
-  if (kStore && slot_new >= 0) stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
+  if (kNew && slot_new >= 0) stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
   // (the barrier that publishes blk_s and tok_s comes after the first tile's
   // loads are issued, below)
 
@@ -414,19 +392,18 @@ void decode_kernel(const DecodeArgs a) {
   };
 
   // The wave holding the newest token takes the tile with position n-1 (the
-  // partition's last) after its other tiles. When the slot is that position's
-  // slot, the wave puts the token into the tile's registers as the pool will
-  // hold it and writes the pool after its last load, so nothing written is
-  // read back in the launch. Any other slot is written as the store kernel
-  // writes it, before the tile is read.
-  const bool has_new = kStore && slot_new >= 0;
+  // partition's last) after its other tiles. When the token's slot is that
+  // position's slot, the wave puts the token into the tile's registers as the
+  // pool will hold it after the store; any other slot is not read by this
+  // sequence (the store launched after the decode writes it), so the tile is
+  // read from the pool as it is.
+  const bool has_new = kNew && slot_new >= 0;
   const int t_end = has_new ? t_new : ntiles;
   // This wave's first tile is loaded before the barrier that publishes blk_s:
   // with blocks of at least one tile it lies in one block, whose id is read
   // straight from the table (a scalar load), so the K/V loads need not wait
-  // for the table to pass through LDS. (Measured 0.5-1.7 % on pa_decode; with
-  // the fused store it cost 1-2 %, so those instances keep the plain order.)
-  const bool early = !kStore && bs >= kTile && w < t_end;
+  // for the table to pass through LDS (measured 0.5-1.7 %).
+  const bool early = bs >= kTile && w < t_end;
   uint4 kr0[kKC], vr0[kVC][kDL];
   if (early) {
     const int id = as_constant(bt)[(w * kTile) / bs];
@@ -444,14 +421,13 @@ void decode_kernel(const DecodeArgs a) {
     load_tile(t, kr, vr);
     compute_tile(t, kr, vr);
   }
-  if constexpr (kStore) {
+  if constexpr (kNew) {
     if (has_new) {
       const int r = n - 1 - (p0 + t_new * kTile);     // the token's key index in the tile
       // uniform by construction; read as a scalar so that the branches below
       // stay uniform for the compiler
       const long long own = (long long)__builtin_amdgcn_readfirstlane(blk_s[(n - 1 - p0) / bs]) * bs + (n - 1) % bs;
       if (own != slot_new) {
-        write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
         uint4 kr[kKC], vr[kVC][kDL];
         load_tile(t_new, kr, vr);
         compute_tile(t_new, kr, vr);
@@ -494,7 +470,6 @@ void decode_kernel(const DecodeArgs a) {
           }
         }
         pv_tile(t_new, vr);
-        write_new_token<kD, kFp8>(a, slot_new, h, lane, tok_s);
       }
     }
   }
@@ -574,10 +549,66 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(
     out[row * kD + threadIdx.x + dl * kWave] = uint16_t(f32_to_bf16(O[dl] / L));
 }
 
+// Longest sequences first. Workgroups are dispatched in grid order; with the
+// sequences in batch order the last ones to start are as long as any, and the
+// launch ends with a tail of long workgroups on a mostly idle chip. Taken
+// longest first, the tail is made of the shortest ones (measured: Qwen3-8B
+// layer 630 -> 613 us, mixed-step decode 188 -> 178 us, with the batch sorted
+// on the host). One workgroup ranks the sequences by their number of 64-key
+// tiles (a counting sort over 1024 buckets; longer contexts share the top
+// bucket): order[rank] = sequence. Sequences of one bucket land in any order;
+// each sequence's result does not depend on which workgroup computes it.
+constexpr int kOrderBuckets = 1024;
+constexpr int kOrderThreads = 1024;   // one bucket per thread
+
+bool decode_orders_sequences(int num_seqs) {
+  return PA_DECODE_ORDER_MIN_SEQS > 0 && num_seqs >= PA_DECODE_ORDER_MIN_SEQS;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* __restrict__ context_lens,
+                                                                     int num_seqs, int ctx_cap,
+                                                                     int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderBuckets];
+  __shared__ int wsum[kOrderThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wv = tid / kWave;
+  auto bucket = [&](int s) {
+    int n = context_lens[s];
+    n = n < ctx_cap ? n : ctx_cap;
+    n = n > 0 ? n : 0;
+    const int t = (n + kTile - 1) / kTile;
+    return kOrderBuckets - 1 - (t < kOrderBuckets - 1 ? t : kOrderBuckets - 1);   // longest first
+  };
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kOrderThreads) atomicAdd(&cnt[bucket(s)], 1);
+  __syncthreads();
+  // exclusive prefix sum of the bucket counts: inclusive scan inside each wave,
+  // then the waves' totals
+  const int c = cnt[tid];
+  int x = c;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[wv] = x;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wv; ++i) base += wsum[i];
+  cnt[tid] = base + x - c;
+  __syncthreads();
+  for (int s = tid; s < num_seqs; s += kOrderThreads) order[atomicAdd(&cnt[bucket(s)], 1)] = s;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts) {
-  if (num_parts <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_q_heads * num_parts;
-  return rows * ((size_t)head_dim + 2) * sizeof(float);
+  const size_t parts = num_parts > 1 ? align256(rows * ((size_t)head_dim + 2) * sizeof(float)) : 0;
+  const size_t ord = decode_orders_sequences(num_seqs) ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+  return parts + ord;
 }
 
 template <int kD, int kG, bool kFp8>
@@ -605,8 +636,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
                          int max_context_len, float scale, uint16_t* out, const PoolDims& pool,
                          const float* k_scale, const float* v_scale, int partition_size,
                          void* workspace, hipStream_t stream, const uint16_t* new_k,
-                         const uint16_t* new_v, const int32_t* new_slots, uint8_t* k_store,
-                         uint8_t* v_store) {
+                         const uint16_t* new_v, const int32_t* new_slots) {
   if (num_seqs == 0) return hipSuccess;
   const int D = pool.head_dim;
   const int G = num_q_heads / pool.num_kv_heads;
@@ -623,11 +653,16 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.out = out;
+  // workspace: the partials (split contexts), then the sequence order
   const size_t rows = (size_t)num_seqs * num_q_heads * NP;
   float* ws = static_cast<float*>(workspace);
   a.part_o = NP > 1 ? ws : nullptr;
   a.part_m = NP > 1 ? ws + rows * D : nullptr;
   a.part_l = NP > 1 ? ws + rows * (D + 1) : nullptr;
+  const size_t part_bytes = NP > 1 ? align256(rows * ((size_t)D + 2) * sizeof(float)) : 0;
+  int32_t* order = decode_orders_sequences(num_seqs)
+                       ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part_bytes) : nullptr;
+  a.order = order;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool.num_kv_heads;
@@ -639,10 +674,13 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
   a.new_k = new_k;
   a.new_v = new_v;
   a.new_slots = new_slots;
-  a.k_store = k_store;
-  a.v_store = v_store;
   a.num_slots = (long long)pool.num_blocks * pool.block_size;
   const unsigned grid = unsigned((long long)num_seqs * pool.num_kv_heads * NP);
+  if (order) {
+    decode_order_kernel<<<1, kOrderThreads, 0, stream>>>(context_lens, num_seqs, ctx_cap, order);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   bool ok;
   if (D == 64)
     ok = pool.fp8 ? launch_decode_g<64, true>(G, a, grid, stream)

@@ -32,8 +32,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
                          int max_context_len, float scale, uint16_t* out, const PoolDims& pool,
                          const float* k_scale, const float* v_scale, int partition_size,
                          void* workspace, hipStream_t stream, const uint16_t* new_k = nullptr,
-                         const uint16_t* new_v = nullptr, const int32_t* new_slots = nullptr,
-                         uint8_t* k_store = nullptr, uint8_t* v_store = nullptr);
+                         const uint16_t* new_v = nullptr, const int32_t* new_slots = nullptr);
 
 hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
                           const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_tables,

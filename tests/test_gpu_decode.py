@@ -425,3 +425,33 @@ def test_wrapper_rejects_bad_arguments():
     with pytest.raises(pa.PaError):
         pa.decode(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, 0.125, 5,
                   partition_size=100)
+
+
+def test_longest_first_order_many_sequences():
+    """From 128 sequences on, a kernel ranks the sequences longest first before
+    the decode. Many equal lengths, empty sequences, split and whole contexts:
+    every sequence against the oracle, and each sequence's output bit-identical
+    when the batch is given in reverse order or below the ranking threshold."""
+    rng = np.random.default_rng(120)
+    lens = [0] * 5 + [1] * 10 + [64] * 40 + [65] * 20 + rng.integers(1, 3000, 125).tolist()
+    lens = [int(x) for x in rng.permutation(lens)]
+    w = W.custom(seed=120, Hq=8, Hkv=2, D=64, bs=32, context_lens=tuple(lens))
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    ref = _oracle_decode(w, kc, vc)
+    outs = {}
+    for ps in (0, 1024):
+        got = host_bits(case.decode(partition_size=ps))
+        assert_close(bf16_f64(got), ref, *TOL["bf16"], what=f"P={ps}")
+        outs[ps] = got
+    # the same sequences in reverse batch order: same bits per sequence
+    import paged_kv_cache_store_amd as pa
+    from tests.gpu_util import dev_bf16, dev_i32
+    rev = pa.decode(dev_bf16(w.q[::-1]), case.k_cache, case.v_cache, dev_i32(w.block_tables[::-1]),
+                    dev_i32(w.context_lens[::-1]), float(w.scale), w.max_context_len)
+    assert np.array_equal(host_bits(rev)[::-1], outs[0])
+    # 100 sequences (no ranking kernel): same bits for those sequences
+    sub = np.arange(100)
+    few = pa.decode(dev_bf16(w.q[sub]), case.k_cache, case.v_cache, dev_i32(w.block_tables[sub]),
+                    dev_i32(w.context_lens[sub]), float(w.scale), w.max_context_len)
+    assert np.array_equal(host_bits(few), outs[0][sub])
