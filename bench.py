@@ -7,7 +7,8 @@ A step is one pass of the path over one synthetic batch, all on one stream:
     307 sequences sharing a 512-token prefix): each sequence's newest token
     stored and its paged context attended. Both ways of doing that are timed
     per call: pa_store_kv then pa_decode, and pa_store_decode (the two in one
-    launch); the step uses the faster (--path fused|separate forces one);
+    launch); each way is timed as a whole step and the faster is the step
+    (--path fused|separate forces one);
   * the mixed chunked-prefill step (--workload 4): pa_store_kv of 4344 new
     tokens, pa_prefill_varlen of 8 chunks of 512 on cached prefixes, pa_decode
     of 248 sequences.
@@ -22,8 +23,9 @@ or the MALL. That flush is timed on its own and subtracted: a graph of
 events on the launch stream. `value` is the step's algorithmic bytes (unique KV
 bytes read by decode and prefill, q/out, tables, plus the store's reads and
 writes) divided by the cold time per step. The `roofline` object is the
-dominant launch (the decode kernel; with the store inside it when the step
-uses pa_store_decode) timed the same way on its own; `prefill_roofline` is
+dominant kernel (the decode kernel, as pa_decode launches it) timed the same
+way on its own; `step_launch` is the pa_store_decode call (the same decode
+kernel, then the store) when the step uses it; `prefill_roofline` is
 the prefill kernel of the mixed chunked-prefill step against the dense bf16
 MFMA peak. `traffic`, `overfetch` and `mfma_util` are read from the committed
 rocprofv3 counter summaries in profiles/ while the kernel's sources are
@@ -296,7 +298,7 @@ def run_steps(st, steps, warmup, path="auto", graph=True, warm=False):
     replays of [flush]; with graph=False the calls are issued eagerly, events
     around each step after its flush. A decode-only step is pa_store_kv +
     pa_decode ("separate") or pa_store_decode ("fused"); path="auto" takes the
-    one whose per-call figures are faster. warm=True adds back-to-back
+    one whose whole step is faster with cold caches. warm=True adds back-to-back
     (warm-cache) figures. Returns a dict."""
     torch = st.torch
     flush = Flush(torch)
@@ -313,12 +315,17 @@ def run_steps(st, steps, warmup, path="auto", graph=True, warm=False):
     torch.cuda.synchronize()
     out = {"ms": {name: cold_launches(st.pa, torch, f, flush, 10, max(3, steps // 4))
                   for name, f in candidates}}
-    ms = out["ms"]
     if st.decode_only:
+        # the two ways of doing the step, each timed as a whole (the separate
+        # store changes what the decode after it reads, so the per-call
+        # figures do not add up to the step)
+        ways = {"fused": [("store_decode", st.store_decode)],
+                "separate": [("store", st.store), ("decode", st.decode)]}
+        out["ms_step_ways"] = {k: cold_launches(st.pa, torch, lambda fs=fs: [f() for _, f in fs], flush, 10,
+                                                max(3, steps // 4)) for k, fs in ways.items()}
         if path == "auto":
-            path = "fused" if ms["store_decode"] <= ms["store"] + ms["decode"] else "separate"
-        calls = ([("store_decode", st.store_decode)] if path == "fused"
-                 else [("store", st.store), ("decode", st.decode)])
+            path = min(ways, key=lambda k: out["ms_step_ways"][k])
+        calls = ways[path]
     else:
         path = "separate"
         calls = candidates
@@ -536,9 +543,10 @@ def decode_entry(r):
     if "store_decode" in ms:
         both = r["decode_bytes"] + r["store_bytes"]
         ent.update({"store_decode_ms": round(ms["store_decode"], 5),
-                    "store_decode_TBps": round(tbps(both, ms["store_decode"]), 4),
-                    "store_plus_decode_ms": round(ms["store"] + ms["decode"], 5),
-                    "store_plus_decode_TBps": round(tbps(both, ms["store"] + ms["decode"]), 4)})
+                    "store_decode_TBps": round(tbps(both, ms["store_decode"]), 4)})
+    if r.get("ms_step_ways"):
+        # each way of doing the decode step timed whole (cold caches)
+        ent["step_ways_ms"] = {k: round(v, 5) for k, v in r["ms_step_ways"].items()}
     if "prefill" in ms:
         tf = r["prefill_flops"] / (ms["prefill"] * 1e-3) / 1e12
         ent.update({"prefill_TFLOPs": round(tf, 2), "prefill_ms": round(ms["prefill"], 5),
@@ -573,7 +581,7 @@ def main():
                     help="decode partition size (default: the workload's, else automatic)")
     ap.add_argument("--path", choices=["auto", "fused", "separate"], default="auto",
                     help="decode-only steps: pa_store_decode (fused), pa_store_kv + pa_decode "
-                         "(separate), or the faster of the two by their per-call figures (auto)")
+                         "(separate), or the faster of the two, each timed as a whole step (auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the figures of the other workloads")
     ap.add_argument("--eager", action="store_true",
@@ -605,7 +613,7 @@ def main():
         t = run_steps(st, steps, warmup, path=path, graph=not args.eager, warm=args.warm)
         dec_b, dec_logical, dec_kv = decode_bytes(w)
         res = {"w": w, "ms_step": t["ms_step"], "step_ms_pct": t.get("step_ms_pct"), "ms": t["ms"],
-               "ms_warm": t.get("ms_warm"), "path": t["path"],
+               "ms_warm": t.get("ms_warm"), "path": t["path"], "ms_step_ways": t.get("ms_step_ways"),
                "ms_step_warm": t.get("ms_step_warm"), "decode_bytes": dec_b,
                "decode_logical": dec_logical, "store_bytes": store_bytes(w), "P": st.P}
         if w.has_prefill:
@@ -619,17 +627,13 @@ def main():
     w = r["w"]
     step_bytes = r["decode_bytes"] + r["store_bytes"] + r.get("prefill_bytes", 0)
     value = step_bytes / (r["ms_step"] * 1e-3) / 1e12
-    # the dominant launch: the decode kernel, with the newest tokens' store in it
-    # when the step uses pa_store_decode
+    # the dominant kernel: the decode (decode_kernel), timed on its own as
+    # pa_decode launches it; pa_store_decode runs the same kernel with the
+    # newest tokens read from its arguments, then the store of those tokens
     whole = r["P"] >= w.max_context_len
-    if r["path"] == "fused":
-        dom_name, dom_bytes = "store_decode", r["decode_bytes"] + r["store_bytes"]
-        dom_kernel = ("decode_kernel with the newest tokens' store (pa_store_decode; contexts whole, no reduce)"
-                      if whole else "decode_kernel with the store + decode_reduce_kernel (pa_store_decode)")
-    else:
-        dom_name, dom_bytes = "decode", r["decode_bytes"]
-        dom_kernel = ("decode_kernel (pa_decode; contexts whole, no reduce)" if whole
-                      else "decode_kernel + decode_reduce_kernel (pa_decode)")
+    dom_name, dom_bytes = "decode", r["decode_bytes"]
+    dom_kernel = ("decode_kernel (as pa_decode launches it; contexts whole, no reduce)" if whole
+                  else "decode_kernel + decode_reduce_kernel (as pa_decode launches them)")
     dec_tbs = tbps(dom_bytes, r["ms"][dom_name])
     traffic = None
     if args.partition_size is None:
@@ -665,6 +669,14 @@ def main():
     }
     if w.number == 3:
         line["roofline"]["logical_GBps"] = round(tbps(r["decode_logical"], r["ms"]["decode"]) * 1e3, 2)
+    if r["path"] == "fused":
+        # the step's decode launch as the step makes it (pa_store_decode: the
+        # decode kernel, then the store of the newest tokens), over its bytes
+        both = r["decode_bytes"] + r["store_bytes"]
+        line["step_launch"] = {"call": "pa_store_decode", "bytes_per_call": both,
+                               "ms_per_call": round(r["ms"]["store_decode"], 5),
+                               "achieved_GBps": round(tbps(both, r["ms"]["store_decode"]) * 1e3, 2),
+                               "frac": round(tbps(both, r["ms"]["store_decode"]) / HBM_PEAK_TBS, 4)}
     if w.has_prefill:
         line["prefill_roofline"] = prefill_roofline(r)
     if args.warm:

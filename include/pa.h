@@ -109,9 +109,10 @@ pa_status pa_store_kv(const void* k, const void* v, const int32_t* slot_mapping,
 
 /* Bytes of device workspace pa_decode needs for these bounds: the split-context
  * partials when a context can span more than one partition, plus, for
- * num_seqs >= 128, the order in which the sequences are processed (longest
- * first, ranked on the device by a small kernel launched before the decode).
- * 0 when neither applies. partition_size as in pa_decode. */
+ * num_seqs >= 128 with max_context_len > 1024, the order in which the
+ * sequences are processed (longest first, ranked on the device by a small
+ * kernel launched before the decode). 0 when neither applies. partition_size
+ * as in pa_decode. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
 
@@ -141,9 +142,10 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  *                 PA_ERR_UNSUPPORTED
  *   workspace     device scratch of at least pa_decode_workspace_size(...) bytes
  *                 (may be NULL when that size is 0); contents on entry ignored.
- *                 With num_seqs >= 128 an extra kernel ranks the sequences by
- *                 context length into it first (longest first), so the launch
- *                 does not end on a tail of long sequences
+ *                 With num_seqs >= 128 and contexts possibly longer than 1024
+ *                 tokens an extra kernel first ranks the sequences by context
+ *                 length into it (longest first), so the launch does not end
+ *                 on a tail of long sequences
  * Query head h reads KV head h / (num_q_heads / num_kv_heads); the group size
  * num_q_heads / num_kv_heads must be 1, 2, 4 or 8. Output: softmax(scale*q.k)
  * weighted sum of v, float32 accumulation, rounded to nearest-even bf16. */

@@ -124,7 +124,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
   const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, ctx, partition_size);
   if (P <= 0) return 0;
   const int32_t np = ctx > 0 ? (ctx + P - 1) / P : 1;
-  return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
+  return pa::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np, ctx);
 }
 
 namespace {
@@ -162,7 +162,7 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   const int32_t P = pa_decode_partition_size(num_seqs, num_q_heads, cap, partition_size);
   if (P / dims.block_size > 256) return PA_ERR_UNSUPPORTED;  // block ids of a partition live in LDS
   const int32_t np = cap > 0 ? (cap + P - 1) / P : 1;
-  const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, dims.head_dim, np);
+  const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, dims.head_dim, np, cap);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
   const hipError_t e = pa::launch_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),

@@ -41,8 +41,12 @@ namespace pa {
 #endif
 
 // Sequences are taken longest first when there are at least this many (0: never)
+// and contexts may be longer than PA_DECODE_ORDER_MIN_CONTEXT tokens
 #ifndef PA_DECODE_ORDER_MIN_SEQS
 #define PA_DECODE_ORDER_MIN_SEQS 128
+#endif
+#ifndef PA_DECODE_ORDER_MIN_CONTEXT
+#define PA_DECODE_ORDER_MIN_CONTEXT 1024
 #endif
 
 constexpr int kDecodeThreads = PA_DECODE_WAVES * 64;
@@ -553,16 +557,21 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(
 // sequences in batch order the last ones to start are as long as any, and the
 // launch ends with a tail of long workgroups on a mostly idle chip. Taken
 // longest first, the tail is made of the shortest ones (measured: Qwen3-8B
-// layer 630 -> 613 us, mixed-step decode 188 -> 178 us, with the batch sorted
-// on the host). One workgroup ranks the sequences by their number of 64-key
-// tiles (a counting sort over 1024 buckets; longer contexts share the top
-// bucket): order[rank] = sequence. Sequences of one bucket land in any order;
-// each sequence's result does not depend on which workgroup computes it.
+// layer 631 -> 621 us, mixed-step decode 187 -> 181 us, its fp8 form 111 ->
+// 98 us). One workgroup ranks the sequences by their number of 64-key tiles (a
+// counting sort over 1024 buckets; longer contexts share the top bucket):
+// order[rank] = sequence. Sequences of one bucket land in any order; each
+// sequence's result does not depend on which workgroup computes it. The
+// ranking launch takes ~5 us, more than the tail costs when contexts are short
+// (Qwen3-0.6B layer, contexts up to 1024: no gain), so it runs only for many
+// sequences whose contexts may be longer than that.
 constexpr int kOrderBuckets = 1024;
 constexpr int kOrderThreads = 1024;   // one bucket per thread
+constexpr int kOrderKeep = 4;         // bucket keys of up to 4096 sequences kept in registers
 
-bool decode_orders_sequences(int num_seqs) {
-  return PA_DECODE_ORDER_MIN_SEQS > 0 && num_seqs >= PA_DECODE_ORDER_MIN_SEQS;
+bool decode_orders_sequences(int num_seqs, int ctx_cap) {
+  return PA_DECODE_ORDER_MIN_SEQS > 0 && num_seqs >= PA_DECODE_ORDER_MIN_SEQS &&
+         ctx_cap > PA_DECODE_ORDER_MIN_CONTEXT;
 }
 
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32_t* __restrict__ context_lens,
@@ -581,8 +590,17 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
     return kOrderBuckets - 1 - (t < kOrderBuckets - 1 ? t : kOrderBuckets - 1);   // longest first
   };
   cnt[tid] = 0;
+  int key[kOrderKeep];
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k) {
+    const int s = tid + k * kOrderThreads;
+    key[k] = s < num_seqs ? bucket(s) : -1;
+  }
   __syncthreads();
-  for (int s = tid; s < num_seqs; s += kOrderThreads) atomicAdd(&cnt[bucket(s)], 1);
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k)
+    if (key[k] >= 0) atomicAdd(&cnt[key[k]], 1);
+  for (int s = tid + kOrderKeep * kOrderThreads; s < num_seqs; s += kOrderThreads) atomicAdd(&cnt[bucket(s)], 1);
   __syncthreads();
   // exclusive prefix sum of the bucket counts: inclusive scan inside each wave,
   // then the waves' totals
@@ -599,15 +617,19 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(const int32
   for (int i = 0; i < wv; ++i) base += wsum[i];
   cnt[tid] = base + x - c;
   __syncthreads();
-  for (int s = tid; s < num_seqs; s += kOrderThreads) order[atomicAdd(&cnt[bucket(s)], 1)] = s;
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k)
+    if (key[k] >= 0) order[atomicAdd(&cnt[key[k]], 1)] = tid + k * kOrderThreads;
+  for (int s = tid + kOrderKeep * kOrderThreads; s < num_seqs; s += kOrderThreads)
+    order[atomicAdd(&cnt[bucket(s)], 1)] = s;
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts) {
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts, int ctx_cap) {
   const size_t rows = (size_t)num_seqs * num_q_heads * num_parts;
   const size_t parts = num_parts > 1 ? align256(rows * ((size_t)head_dim + 2) * sizeof(float)) : 0;
-  const size_t ord = decode_orders_sequences(num_seqs) ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
+  const size_t ord = decode_orders_sequences(num_seqs, ctx_cap) ? align256((size_t)num_seqs * sizeof(int32_t)) : 0;
   return parts + ord;
 }
 
@@ -660,7 +682,7 @@ hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_
   a.part_m = NP > 1 ? ws + rows * D : nullptr;
   a.part_l = NP > 1 ? ws + rows * (D + 1) : nullptr;
   const size_t part_bytes = NP > 1 ? align256(rows * ((size_t)D + 2) * sizeof(float)) : 0;
-  int32_t* order = decode_orders_sequences(num_seqs)
+  int32_t* order = decode_orders_sequences(num_seqs, ctx_cap)
                        ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part_bytes) : nullptr;
   a.order = order;
   a.max_blocks_per_seq = max_blocks_per_seq;

@@ -24,7 +24,9 @@ hipError_t launch_copy_blocks(uint8_t* k_cache, uint8_t* v_cache, const int32_t*
 //   float o[num_seqs][num_q_heads][num_parts][head_dim]   (unnormalised partial output)
 //   float m[num_seqs][num_q_heads][num_parts]              (partial max, log2 units)
 //   float l[num_seqs][num_q_heads][num_parts]              (partial sum of weights)
-size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts);
+//   int32 order[num_seqs] (256-byte aligned, after the partials) when the
+//   sequences are ranked longest first (many sequences, long contexts)
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int num_parts, int ctx_cap);
 
 hipError_t launch_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
                          const int32_t* block_tables, int max_blocks_per_seq,
