@@ -156,6 +156,30 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const pa_cache_desc* cache, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the device scratch array behind pa_decode_noalloc, per GPU. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pa_decode_noalloc — pa_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments as pa_decode without the workspace; same kernels,
+ * same results bit for bit. The scratch pa_decode would take from the
+ * workspace (pa_decode_workspace_size bytes: split-context partials, the
+ * sequence order) comes from a device array of PA_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library, one per GPU the library runs on, held until the
+ * process ends; a call that would need more returns PA_ERR_WORKSPACE before
+ * enqueuing anything. The call allocates nothing. The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress) with that device
+ * current. Every call on a GPU shares that GPU's array and it keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other
+ * threads) race and their results are undefined; calls on one stream are
+ * ordered and safe. No scratch byte needs to start at zero: a call writes
+ * every scratch byte it reads. */
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* out,
+                            const pa_cache_desc* cache, int32_t partition_size, hipStream_t stream);
+
 /* pa_store_decode — a decode step: pa_store_kv of each sequence's newest token
  * and pa_decode, in one call (the store and the decode are the two halves of a
  * decode step: "Nano-vLLM…", 三.1 and 三.3).

@@ -16,7 +16,7 @@ import re
 
 import torch
 
-__all__ = ["store_kv", "decode", "prefill_varlen", "add_rmsnorm", "decode_workspace_size",
+__all__ = ["store_kv", "decode", "decode_noalloc", "prefill_varlen", "add_rmsnorm", "decode_workspace_size",
            "decode_partition_size", "empty_pools", "capture_step", "copy_blocks", "BlockManager",
            "PaError", "LIB_PATH", "library"]
 
@@ -72,9 +72,11 @@ def _load():
     lib.pa_decode_partition_size.restype = I32
     lib.pa_decode.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
     lib.pa_store_decode.argtypes = [P, P, P, P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P, SZ, P]
+    lib.pa_decode_noalloc.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P]
     lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
     lib.pa_add_rmsnorm.argtypes = [P, P, P, I32, I32, F, P, P, P]
-    for name in ("pa_store_kv", "pa_decode", "pa_store_decode", "pa_prefill_varlen", "pa_add_rmsnorm"):
+    for name in ("pa_store_kv", "pa_decode", "pa_store_decode", "pa_prefill_varlen", "pa_add_rmsnorm",
+                 "pa_decode_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     I64, PI32, PI64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -252,6 +254,29 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_l
                         _stream(stream))
     if st != 0:
         raise PaError(st, "pa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, out,
+                   k_scale=None, v_scale=None, partition_size=0, stream=None):
+    """pa_decode_noalloc: pa_decode with its scratch in the library's device
+    array (no workspace, nothing allocated). `out` ([S, Hq, D] bf16) is
+    required. Calls that overlap on one GPU race (see include/pa.h)."""
+    desc, nb, hkv, d, bs = _pool_desc(k_cache, v_cache, k_scale, v_scale)
+    dev = k_cache.device
+    _check(q, "q", torch.bfloat16, 3, dev)
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    _check(context_lens, "context_lens", torch.int32, 1, dev)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    S, hq, dq = q.shape
+    if dq != d or block_tables.shape[0] != S or context_lens.numel() != S or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q [S, Hq, D], block_tables [S, MB], context_lens [S] and out disagree")
+    st = library().pa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                     block_tables.shape[1], _ptr(context_lens), S, hq, int(max_context_len),
+                                     float(scale), _ptr(out), ctypes.byref(desc), int(partition_size),
+                                     _stream(stream))
+    if st != 0:
+        raise PaError(st, "pa_decode_noalloc")
     return out
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "pa.h"
 #include "pa_block_manager.h"
 #include "pa_launch.h"
@@ -40,6 +42,46 @@ pa_status check_cache(const pa_cache_desc* c, pa::PoolDims* dims) {
 }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+}  // namespace
+
+// Scratch of pa_decode_noalloc: a file-scope device array, one per GPU, held
+// until the process ends. In host code `scratch` is only the symbol's
+// stand-in; kernels are given its device address on the device concerned,
+// looked up once per device with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the null stream), looked up the first time with that device current.
+pa_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
 
 // The kernels move bf16 / fp8 data in 16-byte vectors and read int32 arrays as
 // dwords: data pointers must be 16-byte aligned, int32 arrays 4-byte aligned.
@@ -138,7 +180,7 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       int32_t max_context_len, float scale, void* out, const pa_cache_desc* cache,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, const void* new_k, const void* new_v,
-                      const int32_t* slot_mapping, bool fused) {
+                      const int32_t* slot_mapping, bool fused, bool noalloc = false) {
   pa::PoolDims dims;
   pa_status st = check_cache(cache, &dims);
   if (st != PA_OK) return st;
@@ -163,7 +205,17 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (P / dims.block_size > 256) return PA_ERR_UNSUPPORTED;  // block ids of a partition live in LDS
   const int32_t np = cap > 0 ? (cap + P - 1) / P : 1;
   const size_t need = pa::decode_workspace_bytes(num_seqs, num_q_heads, dims.head_dim, np, cap);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  if (noalloc) {
+    // the library's own scratch array instead of a caller's workspace
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    workspace = nullptr;
+    if (need > 0) {
+      const pa_status st2 = scratch_address(stream, &workspace);
+      if (st2 != PA_OK) return st2;
+    }
+  } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+    return PA_ERR_WORKSPACE;
+  }
   const hipError_t e = pa::launch_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
       static_cast<const uint8_t*>(v_cache), block_tables, max_blocks_per_seq, context_lens, num_seqs,
@@ -189,6 +241,16 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      num_q_heads, max_context_len, scale, out, cache, partition_size, workspace,
                      workspace_bytes, stream, nullptr, nullptr, nullptr, false);
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* out,
+                            const pa_cache_desc* cache, int32_t partition_size, hipStream_t stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_q_heads, max_context_len, scale, out, cache, partition_size, nullptr, 0, stream,
+                     nullptr, nullptr, nullptr, false, true);
 }
 
 pa_status pa_store_decode(const void* q, const void* new_k, const void* new_v,

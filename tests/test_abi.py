@@ -78,6 +78,25 @@ def test_decode_validation(lib):
     assert decode(lib, desc(bs=16), maxctx=8192, mb=512, P=8192, ws=FAKE, wsb=1 << 30) == UNSUP
 
 
+def decode_noalloc(lib, d, q=FAKE, S=4, hq=4, maxctx=100, mb=8, P=0, scale=0.125):
+    return lib.pa_decode_noalloc(q, FAKE, FAKE, FAKE, mb, FAKE, S, hq, maxctx, scale, FAKE,
+                                 ctypes.byref(d) if d is not None else None, P, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode checks its arguments as pa_decode does, and
+    refuses a call whose scratch would exceed the library's array (64 MiB)
+    before anything runs."""
+    assert decode_noalloc(lib, None) == NULL
+    assert decode_noalloc(lib, desc(), q=None) == NULL
+    assert decode_noalloc(lib, desc(), hq=3) == SHAPE
+    assert decode_noalloc(lib, desc(), P=100) == SHAPE
+    assert decode_noalloc(lib, desc(), S=0, q=None) == OK
+    big = desc(nb=8, bs=256, hkv=8, d=128)
+    assert lib.pa_decode_workspace_size(4096, 32, 128, 32768, 256) > (64 << 20)
+    assert decode_noalloc(lib, big, S=4096, hq=32, maxctx=32768, mb=128, P=256) == WS
+
+
 def store_decode(lib, d, nk=FAKE, nv=FAKE, sm=FAKE, S=4, hq=4, maxctx=100, mb=8, P=0):
     return lib.pa_store_decode(FAKE, nk, nv, sm, FAKE, FAKE, FAKE, mb, FAKE, S, hq, maxctx, 0.125,
                                FAKE, ctypes.byref(d) if d is not None else None, P, None, 0, None)
