@@ -652,7 +652,8 @@ def main():
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
                                    f"mean {float(w.context_lens.mean()):.1f}",
                    "kv_dtype": w.kv_dtype, "partition_size": r["P"], "parallelism": "single GPU",
-                   "step_path": ("pa_store_decode (store inside the decode launch)" if r["path"] == "fused"
+                   "step_path": ("pa_store_decode (the decode, taking the newest tokens from its arguments, "
+                                 "then their store)" if r["path"] == "fused"
                                  else "pa_store_kv then pa_decode" + (" (+ pa_prefill_varlen)"
                                                                       if w.has_prefill else "")),
                    "launch": "eager calls" if args.eager else "one HIP-graph replay per step",
