@@ -455,3 +455,17 @@ def test_longest_first_order_many_sequences():
     few = pa.decode(dev_bf16(w.q[sub]), case.k_cache, case.v_cache, dev_i32(w.block_tables[sub]),
                     dev_i32(w.context_lens[sub]), float(w.scale), w.max_context_len)
     assert np.array_equal(host_bits(few), outs[0][sub])
+
+
+def test_longest_first_order_beyond_register_keys():
+    """More than 4096 sequences: the ranking keeps the first 4096 bucket keys in
+    registers and recomputes the rest; every sequence against the oracle."""
+    rng = np.random.default_rng(121)
+    lens = rng.integers(1, 40, 5000).tolist()
+    lens[4321] = 1500                       # one long context: the ranking runs
+    lens[17] = 0
+    w = W.custom(seed=121, Hq=2, Hkv=1, D=64, bs=16, context_lens=tuple(int(x) for x in lens))
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    got = bf16_f64(host_bits(case.decode(partition_size=0)))
+    assert_close(got, _oracle_decode(w, kc, vc), *TOL["bf16"], what="5000 sequences")
