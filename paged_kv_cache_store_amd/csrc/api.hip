@@ -180,7 +180,7 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       int32_t max_context_len, float scale, void* out, const pa_cache_desc* cache,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, const void* new_k, const void* new_v,
-                      const int32_t* slot_mapping, bool fused, bool noalloc = false) {
+                      const int32_t* slot_mapping, bool with_new, bool noalloc = false) {
   pa::PoolDims dims;
   pa_status st = check_cache(cache, &dims);
   if (st != PA_OK) return st;
@@ -192,11 +192,11 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
-  if (fused && (!new_k || !new_v || !slot_mapping)) return PA_ERR_NULL;
+  if (with_new && (!new_k || !new_v || !slot_mapping)) return PA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(workspace, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PA_ERR_UNSUPPORTED;
-  if (fused && (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(slot_mapping, 4)))
+  if (with_new && (!aligned(new_k, 16) || !aligned(new_v, 16) || !aligned(slot_mapping, 4)))
     return PA_ERR_UNSUPPORTED;
   // the grid covers contexts up to the smaller of the two host bounds
   const long long cap_ll = (long long)max_blocks_per_seq * dims.block_size;
@@ -220,9 +220,9 @@ pa_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
       static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_cache),
       static_cast<const uint8_t*>(v_cache), block_tables, max_blocks_per_seq, context_lens, num_seqs,
       num_q_heads, cap, scale, static_cast<uint16_t*>(out), dims, cache->k_scale, cache->v_scale, P,
-      workspace, stream, fused ? static_cast<const uint16_t*>(new_k) : nullptr,
-      fused ? static_cast<const uint16_t*>(new_v) : nullptr, fused ? slot_mapping : nullptr);
-  if (e != hipSuccess || !fused) return hip_status(e);
+      workspace, stream, with_new ? static_cast<const uint16_t*>(new_k) : nullptr,
+      with_new ? static_cast<const uint16_t*>(new_v) : nullptr, with_new ? slot_mapping : nullptr);
+  if (e != hipSuccess || !with_new) return hip_status(e);
   // the store of the newest tokens, after the decode that took them from new_k / new_v
   return hip_status(pa::launch_store_kv(static_cast<const uint16_t*>(new_k), static_cast<const uint16_t*>(new_v),
                                         slot_mapping, num_seqs, static_cast<uint8_t*>(const_cast<void*>(k_cache)),
