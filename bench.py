@@ -527,6 +527,13 @@ def copy_calibration(torch, reps):
 
 
 # ---------------------------------------------------------------- main
+def device_info(torch):
+    """The GPU the figures come from (name, architecture, compute units, memory)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+
+
 def tbps(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e12
 
@@ -647,6 +654,7 @@ def main():
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3 KV, bf16 q/out",
         "data": "synthetic (seeded; bf16 N(0,1) q/k/v, random block permutation)",
+        "device": device_info(torch),
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": f"U[{int(w.context_lens.min())},{int(w.context_lens.max())}] "
