@@ -155,14 +155,20 @@ void prefill_kernel(const PrefillArgs a) {
   // within a sequence the later query blocks (they see more keys) first. Every
   // workgroup ranks the sequences itself from cu_k, staged in ids_s (not yet in
   // use); past kSortMax sequences they are taken in reverse index order.
+  // The ranking pass also stages every sequence's query offset and length, so
+  // the chosen sequence's are read from LDS, not with one more round trip.
   const int qb = a.num_qblocks - 1 - rest % a.num_qblocks;
   const int want = rest / a.num_qblocks;           // rank of this workgroup's sequence
   int s = a.num_seqs - 1 - want;
+  int q0, Lq, Lk;
   if (a.num_seqs > 1 && a.num_seqs <= kSortMax) {
     const int S = a.num_seqs;
     for (int i = tid; i < S; i += kPrefillThreads) {
       const int lk = a.cu_k[i + 1] - a.cu_k[i];
+      const int qa = a.cu_q[i];
       ids_s[i] = lk < a.cap_k ? lk : a.cap_k;
+      ids_s[kSortMax + i] = qa;
+      ids_s[2 * kSortMax + i] = a.cu_q[i + 1] - qa;
     }
     __syncthreads();
     for (int i = tid; i < S; i += kPrefillThreads) {
@@ -176,18 +182,21 @@ void prefill_kernel(const PrefillArgs a) {
     }
     __syncthreads();
     s = ids_s[kIdCache - 1];
+    Lk = ids_s[s];
+    q0 = ids_s[kSortMax + s];
+    Lq = ids_s[2 * kSortMax + s];
     __syncthreads();                                // ids_s is reused for block ids
+  } else {
+    q0 = a.cu_q[s];
+    Lq = a.cu_q[s + 1] - q0;
+    Lk = a.cu_k[s + 1] - a.cu_k[s];
+    Lk = Lk < a.cap_k ? Lk : a.cap_k;
   }
+  Lq = Lq < a.max_seqlen_q ? Lq : a.max_seqlen_q;
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   const int l32 = lane % 32;
   const int half = lane / 32;
-
-  const int q0 = a.cu_q[s];
-  int Lq = a.cu_q[s + 1] - q0;
-  Lq = Lq < a.max_seqlen_q ? Lq : a.max_seqlen_q;
-  int Lk = a.cu_k[s + 1] - a.cu_k[s];
-  Lk = Lk < a.cap_k ? Lk : a.cap_k;
   const int row0 = qb * kBM;
   if (row0 >= Lq || Lq <= 0) return;
   const int bs = a.block_size;
@@ -726,11 +735,12 @@ void prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + g4 * 8 + half * 4;
-          const uint32_t b0 = f32_to_bf16(o[db][nb][4 * g4 + 0] * inv);
-          const uint32_t b1 = f32_to_bf16(o[db][nb][4 * g4 + 1] * inv);
-          const uint32_t b2 = f32_to_bf16(o[db][nb][4 * g4 + 2] * inv);
-          const uint32_t b3 = f32_to_bf16(o[db][nb][4 * g4 + 3] * inv);
-          *reinterpret_cast<uint2*>(op + d) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          // v_cvt_pk_bf16_f32: round to nearest even
+          const f32x2_t lo = {o[db][nb][4 * g4 + 0] * inv, o[db][nb][4 * g4 + 1] * inv};
+          const f32x2_t hi = {o[db][nb][4 * g4 + 2] * inv, o[db][nb][4 * g4 + 3] * inv};
+          *reinterpret_cast<uint2*>(op + d) =
+              make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
         }
     }
   }
