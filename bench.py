@@ -115,7 +115,9 @@ def prefill_work(w):
 
 
 # The kernel sources each call's counter figures depend on.
-CALL_SOURCES = {"decode": ("decode.hip", "pa_device.h"), "store_decode": ("decode.hip", "pa_device.h"),
+# the sources of each call's kernels (pa_store_decode: the decode kernel, then the store kernel)
+CALL_SOURCES = {"decode": ("decode.hip", "pa_device.h"),
+                "store_decode": ("decode.hip", "store_kv.hip", "pa_device.h"),
                 "prefill": ("prefill.hip", "pa_device.h"), "store": ("store_kv.hip", "pa_device.h")}
 
 

@@ -188,11 +188,17 @@ __global__ __launch_bounds__(256) void store_kv_chunk_kernel(
         }
       }
     } else {
-      const uint4 vr = *reinterpret_cast<const uint4*>(v + src);
-      const uint32_t w[4] = {vr.x, vr.y, vr.z, vr.w};
+      // one 2-byte value per 16-byte unit. Lane c writes head-dims c,
+      // c + chunks, ..., c + 7 chunks, so that for each e the lanes of a wave
+      // write neighbouring units of the token's rows (a few lines per
+      // instruction) instead of one unit in each of 64 lines
+      const uint16_t* vt = v + (t * num_kv_heads + h) * head_dim;
+      uint16_t* vu = reinterpret_cast<uint16_t*>(v_cache) + v_dst;
+      uint16_t val[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vc[e * kX] = uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+      for (int e = 0; e < 8; ++e) val[e] = vt[c + e * chunks];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vu[(long long)(c + e * chunks) * kX] = val[e];
     }
   } else {
     const float ks = k_scale[h];

@@ -62,5 +62,6 @@ def test_profile_figures_follow_the_kernel_sources(tmp_path):
     assert bench.profile_figure(str(p), "traffic_bytes_per_launch", 2, "decode") is None
     assert bench.profile_figure(str(p), "traffic_bytes_per_launch", 4, "prefill") is None
     assert bench.profile_figure(str(tmp_path / "missing.md"), "traffic_bytes_per_launch", 3, "decode") is None
-    assert bench.sources_sha256("decode") == bench.sources_sha256("store_decode")
+    # pa_store_decode runs the decode kernel and then the store kernel
+    assert bench.sources_sha256("decode") != bench.sources_sha256("store_decode")
     assert bench.sources_sha256("decode") != bench.sources_sha256("prefill")
