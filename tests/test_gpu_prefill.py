@@ -49,7 +49,11 @@ def test_prefill_equal_lengths_and_many_sequences():
     sequences) they are taken by index. Every row against the oracle."""
     rng = np.random.default_rng(330)
     for pf in ([(40, 24)] * 5 + [(0, 64)] * 3 + [(64, 1)],
-               [(int(rng.integers(0, 40)), int(rng.integers(1, 9))) for _ in range(300)]):
+               [(int(rng.integers(0, 40)), int(rng.integers(1, 9))) for _ in range(300)],
+               # the ranked limit exactly, and one past it: each sequence's query
+               # offset and length come from the ranking pass, or from global memory
+               [(int(rng.integers(0, 30)), int(rng.integers(1, 6))) for _ in range(256)],
+               [(int(rng.integers(0, 30)), int(rng.integers(1, 6))) for _ in range(257)]):
         w = W.custom(seed=331, Hq=4, Hkv=2, D=64, bs=16, context_lens=(), prefill=pf)
         print(f"{len(pf)} sequences", flush=True)
         case = GpuCase(w)
