@@ -38,9 +38,12 @@ namespace pa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
+// 32-column blocks per wave. With 2 the pipelined loop needs more than the 512
+// registers of one wave per SIMD (it spills to scratch), so 1 is the built form.
 #ifndef PA_PREFILL_NB
 #define PA_PREFILL_NB 1
 #endif
+// waves per SIMD the register budget is set for (228 VGPRs: 2)
 #ifndef PA_PREFILL_WAVES_PER_EU
 #define PA_PREFILL_WAVES_PER_EU 2
 #endif
