@@ -545,7 +545,9 @@ void prefill_kernel(const PrefillArgs a) {
       const bool grow = mt > m[nb] + 8.f;
       if (__any(grow)) {
         const float mn = grow ? mt : m[nb];
-        const float alpha = fast_exp2(m[nb] - mn);  // 0 the first time (O, l are 0)
+        // 0 the first time (O, l are 0); 1 for a column whose max stays (also
+        // one that has seen no key yet: m = -inf, where m - mn would be NaN)
+        const float alpha = grow ? fast_exp2(m[nb] - mn) : 1.f;
         lsum[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < kDB; ++db)

@@ -62,6 +62,26 @@ def test_prefill_equal_lengths_and_many_sequences():
         assert_close(got, _oracle_prefill(w, kc, vc), *TOL, what=f"{len(pf)} sequences")
 
 
+
+@pytest.mark.parametrize("kv,bs", [("bf16", 16), ("bf16", 256), ("fp8", 64)])
+def test_prefill_rows_without_keys(kv, bs):
+    """Fewer keys than queries: query i sits at position Lk-Lq+i, so the first
+    Lq-Lk rows see no key and are zeros, next to rows of the same workgroup that
+    do see keys (the running-max rescale must leave a column with no key yet
+    untouched); a sequence with no keys at all gives zero rows."""
+    w = W.custom(seed=349, Hq=8, Hkv=2, D=128, bs=bs, context_lens=(), kv_dtype=kv,
+                 prefill=[(0, 100), (0, 70), (40, 90), (0, 5), (10, 300)])
+    lk = np.diff(w.cu_seqlens_k).astype(np.int64)
+    lk[0], lk[1], lk[3] = 60, 0, 2
+    w.cu_seqlens_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    print(f"{kv} block {bs}: keys per sequence {lk.tolist()}", flush=True)
+    case = GpuCase(w)
+    kc, vc = oracle_pools(w)
+    got = bf16_f64(host_bits(case.prefill()))
+    assert_close(got, _oracle_prefill(w, kc, vc), *(TOL_FP8 if kv == "fp8" else TOL), what="prefill")
+    q0, q1 = int(w.cu_seqlens_q[1]), int(w.cu_seqlens_q[2])
+    assert not np.any(got[q0:q1]) and not np.any(got[:40]) and not np.any(got[260:263])
+
 FP8_CASES = [
     dict(seed=321, Hq=4, Hkv=1, D=128, bs=16, prefill=[(0, 1), (0, 17), (0, 64), (0, 65), (16, 16)]),
     dict(seed=322, Hq=8, Hkv=2, D=128, bs=64, prefill=[(100, 30), (37, 200), (0, 300)]),
