@@ -571,7 +571,7 @@ def prefill_roofline(r):
     tf = r["prefill_flops"] / (ms * 1e-3) / 1e12
     mfma = profile_figure(MFMA_PROFILE, "mfma_util", w.number, "prefill")
     traffic = profile_figure(TRAFFIC_PROFILE, "traffic_bytes_per_launch", w.number, "prefill")
-    return {"bound": "mfma", "workload": w.name, "kernel": "prefill_kernel (pa_prefill_varlen)",
+    return {"bound": "mfma", "workload": w.name, "kernel": "prefill_persist_kernel (pa_prefill_varlen)",
             "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops_per_launch": r["prefill_flops"],
             "ms_per_launch": round(ms, 5), "mfma_util": mfma,

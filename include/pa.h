@@ -243,6 +243,23 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                             int32_t max_seqlen_k, float scale, void* out,
                             const pa_cache_desc* cache, hipStream_t stream);
 
+/* pa_prefill_set_slots — how many workgroups a pa_prefill_varlen launch over a
+ * bf16 pool with blocks of at least 64 tokens keeps resident. That launch is
+ * persistent: each workgroup takes a run of work items (sequence, KV head,
+ * block of query rows) and starts the next item's copies while it finishes the
+ * current one, so the per-item start-up latency (block ids, first K/V tiles,
+ * Q rows) is paid once per workgroup instead of once per item (chunked
+ * prefill, "nano-vllm-lite…", 核心技术改进 §2: prefill is compute-bound, so
+ * the matrix cores are kept busy across items).
+ *   slots  0 (the default): two per compute unit, what the kernel's registers
+ *          and LDS allow; > 0: that many; < 0: no persistent launch (one
+ *          workgroup per work item, the other paths' kernel).
+ * The output is the same bit for bit for every setting (each item's tiles are
+ * visited in the same order with the same arithmetic). The setting is
+ * process-wide, read at each later launch; it is not synchronised with launches
+ * on other host threads. Always PA_OK. */
+pa_status pa_prefill_set_slots(int32_t slots);
+
 /* pa_add_rmsnorm — residual add fused with RMSNorm in one pass over each row, so
  * the sum is normalised without a round trip through memory ("nano-vllm-lite…",
  * 核心技术改进 §1):

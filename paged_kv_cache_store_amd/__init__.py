@@ -16,7 +16,8 @@ import re
 
 import torch
 
-__all__ = ["store_kv", "decode", "decode_noalloc", "prefill_varlen", "add_rmsnorm", "decode_workspace_size",
+__all__ = ["store_kv", "decode", "decode_noalloc", "prefill_varlen", "prefill_set_slots", "add_rmsnorm",
+           "decode_workspace_size",
            "decode_partition_size", "empty_pools", "capture_step", "copy_blocks", "BlockManager",
            "PaError", "LIB_PATH", "library"]
 
@@ -75,8 +76,9 @@ def _load():
     lib.pa_decode_noalloc.argtypes = [P, P, P, P, I32, P, I32, I32, I32, F, P, D, I32, P]
     lib.pa_prefill_varlen.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, F, P, D, P]
     lib.pa_add_rmsnorm.argtypes = [P, P, P, I32, I32, F, P, P, P]
+    lib.pa_prefill_set_slots.argtypes = [I32]
     for name in ("pa_store_kv", "pa_decode", "pa_store_decode", "pa_prefill_varlen", "pa_add_rmsnorm",
-                 "pa_decode_noalloc"):
+                 "pa_decode_noalloc", "pa_prefill_set_slots"):
         getattr(lib, name).restype = ctypes.c_int
     I64, PI32, PI64 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     lib.pa_copy_blocks.argtypes = [P, P, P, I32, D, P]
@@ -278,6 +280,13 @@ def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, max_c
     if st != 0:
         raise PaError(st, "pa_decode_noalloc")
     return out
+
+
+def prefill_set_slots(slots: int) -> None:
+    """Resident workgroups of a persistent prefill launch (bf16 pool, blocks of at
+    least 64 tokens): 0 = two per compute unit (default), > 0 = that many, < 0 = one
+    workgroup per work item. Process-wide; the output is the same for every value."""
+    library().pa_prefill_set_slots(int(slots))
 
 
 def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, scale,

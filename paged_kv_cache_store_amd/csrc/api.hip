@@ -313,6 +313,11 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
                                        stream));
 }
 
+pa_status pa_prefill_set_slots(int32_t slots) {
+  pa::set_prefill_slots(slots);
+  return PA_OK;
+}
+
 pa_status pa_add_rmsnorm(const void* x, const void* residual, const void* weight, int32_t num_tokens,
                          int32_t hidden, float eps, void* out, void* residual_out, hipStream_t stream) {
   if (num_tokens < 0 || hidden <= 0) return PA_ERR_SHAPE;

@@ -28,6 +28,11 @@
 //   sequence's keys contiguous from row cu_k[s]) take the register path: K
 //   chunks are copied as they are, V is transposed 8 keys x 8 head-dims at a
 //   time into the same LDS layouts, so the MFMA loop is unchanged.
+// * a bf16 pool with blocks of at least one tile (up to kSortMax sequences)
+//   runs the persistent form (prefill_persist_kernel): the same work items and
+//   the same tile loop, with at most two workgroups per CU each running a run
+//   of items, the next item's first tiles copied during the current item's last
+//   steps; its output is bit-identical to one workgroup per item.
 #include <math.h>
 
 #include "pa_device.h"
@@ -751,6 +756,534 @@ void prefill_kernel(const PrefillArgs a) {
   }
 }
 
+// ---- Persistent form of the bf16 block-table path (blocks of at least one tile,
+// at most kSortMax sequences). One launch keeps at most two workgroups per CU
+// resident; each takes a run of work items (sequence, KV head, query block) and
+// passes from one to the next without draining its copy pipeline: the first K
+// tiles and the first V tile of the next item are copied during the current
+// item's last steps, with block ids from an LDS window that was filled while
+// earlier items ran (three windows: the current item's, the next one's and the
+// one after). The items keep the longest-first ranking of the
+// one-item-per-workgroup kernel and are dealt in rounds of one per workgroup,
+// each round in the reverse workgroup order of the one before, so that a
+// workgroup given a long item early gets a short one late. Reversal is by
+// groups of 8 workgroups when the count allows, which keeps the residue of a
+// workgroup index mod 8 (and with 8 KV heads, the KV head an XCD serves) the
+// same in every round.
+constexpr int kWin = 256;   // block ids per window (LDS: 3 windows; longer items refill theirs)
+
+template <int kD, int kG>
+__global__ __launch_bounds__(kPrefillThreads)
+__attribute__((amdgpu_waves_per_eu(2)))
+void prefill_persist_kernel(const PrefillArgs a, int num_items) {
+  constexpr int kBM = kPrefillWaves * 32 / kG;   // query rows per item
+  constexpr int kKS = kD / 16;
+  constexpr int kDB = kD / 32;
+  constexpr int kKC = kD / 8;
+  constexpr int kKW = kKC / kPrefillWaves;
+  constexpr int kVW = (kBN / 8) * (kD / 64) / kPrefillWaves;
+  static_assert(kWin % kPrefillThreads == 0, "window fill is whole rounds of the workgroup");
+
+  __shared__ uint4 k_a[kKC][kBN], k_b[kKC][kBN];
+  __shared__ uint4 v_a[kBN / 8][kD], v_b[kBN / 8][kD];
+  __shared__ int win[3 * kWin];   // three windows of block ids, kWin apart
+  __shared__ int seq_lk[kSortMax], seq_q0[kSortMax], seq_lq[kSortMax], seq_at[kSortMax];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int l32 = lane % 32;
+  const int half = lane / 32;
+  const int col = w * 32 + l32;   // this lane's packed (head, row) column of an item
+  const int Hkv = a.num_kv_heads;
+  const int S = a.num_seqs;
+  const int bshift = a.block_shift;
+  const int bmask = a.block_size - 1;
+  const int slab16 = a.block_size * kD * 2 / 16;   // one KV head's slab of a block, 16-byte units
+  const int blk16 = Hkv * slab16;                  // one block
+  const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache);
+  const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache);
+  const float sc = a.scale_log2;
+
+  // ---- sequences ranked by key count once per workgroup (ties by index)
+  for (int i = tid; i < S; i += kPrefillThreads) {
+    const int lk = a.cu_k[i + 1] - a.cu_k[i];
+    const int qa = a.cu_q[i];
+    seq_lk[i] = lk < a.cap_k ? lk : a.cap_k;
+    seq_q0[i] = qa;
+    const int lq = a.cu_q[i + 1] - qa;
+    seq_lq[i] = lq < a.max_seqlen_q ? lq : a.max_seqlen_q;
+  }
+  __syncthreads();
+  for (int i = tid; i < S; i += kPrefillThreads) {
+    const int li = seq_lk[i];
+    int rank = 0;
+    for (int j = 0; j < S; ++j) {
+      const int lj = seq_lk[j];
+      rank += (lj > li) || (lj == li && j < i);
+    }
+    seq_at[rank] = i;
+  }
+  __syncthreads();
+
+  // ---- work items: rank r -> KV head, query block, sequence (by its rank).
+  // nt: tiles of 64 keys the item reads (0: its rows see no key; < 0: no rows)
+  struct Item { int s, hk, q0, Lq, Lk, row0, nt; };
+  auto item_info = [&](int r) __attribute__((always_inline)) {
+    Item it;
+    it.hk = r % Hkv;
+    const int rest = r / Hkv;
+    it.row0 = (a.num_qblocks - 1 - rest % a.num_qblocks) * kBM;
+    it.s = __builtin_amdgcn_readfirstlane(seq_at[rest / a.num_qblocks]);
+    it.Lk = __builtin_amdgcn_readfirstlane(seq_lk[it.s]);
+    it.q0 = __builtin_amdgcn_readfirstlane(seq_q0[it.s]);
+    it.Lq = __builtin_amdgcn_readfirstlane(seq_lq[it.s]);
+    if (it.row0 >= it.Lq || it.Lq <= 0) {
+      it.nt = -1;
+    } else {
+      int last = it.Lk - it.Lq + (it.row0 + kBM - 1 < it.Lq - 1 ? it.row0 + kBM - 1 : it.Lq - 1);
+      last = last < it.Lk - 1 ? last : it.Lk - 1;
+      it.nt = last >= 0 ? (last + kBN) / kBN : 0;
+    }
+    return it;
+  };
+  // the item of round k for this workgroup (rounds alternate direction)
+  const int P = gridDim.x;
+  const int b = blockIdx.x;
+  auto rank_at = [&](int k) __attribute__((always_inline)) {
+    int idx = b;
+    if (k & 1) idx = P % 8 == 0 ? (P / 8 - 1 - b / 8) * 8 + b % 8 : P - 1 - b;
+    return (long long)k * P + idx;
+  };
+  // this lane's output row of an item (nullptr past the item's rows)
+  auto out_row = [&](const Item& it) __attribute__((always_inline)) -> uint16_t* {
+    const int qr = it.row0 + col % kBM;
+    if (qr >= it.Lq) return nullptr;
+    return a.out + ((long long)(it.q0 + qr) * a.num_q_heads + it.hk * kG + col / kBM) * kD;
+  };
+  // the round of the first item at or after round k that reads keys (-1: none);
+  // items whose rows see no key are written as zeros on the way
+  auto find_item = [&](int k) __attribute__((always_inline)) {
+    for (;; ++k) {
+      const long long r = rank_at(k);
+      if (r >= num_items) return -1;
+      const Item it = item_info(int(r));
+      if (it.nt > 0) return k;
+      if (it.nt == 0) {
+        uint16_t* op = out_row(it);
+        if (op) {
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) *reinterpret_cast<uint2*>(op + db * 32 + g4 * 8 + half * 4) = make_uint2(0u, 0u);
+        }
+      }
+    }
+  };
+  // blocks an item's tiles touch
+  auto item_blocks = [&](int nt, int Lk) __attribute__((always_inline)) {
+    const int lastk = (nt * kBN < Lk ? nt * kBN : Lk) - 1;
+    return (lastk >> bshift) + 1;
+  };
+  // copy the first kWin block ids of the item of round k into window wi
+  // (global_load_lds: the ids land without passing through registers; the
+  // next barrier waits for them)
+  auto window_dma = [&](int k, int wi) __attribute__((always_inline)) {
+    const Item it = item_info(int(rank_at(k)));
+    const int* row = a.block_tables + (long long)it.s * a.max_blocks_per_seq;
+    const int nblk = item_blocks(it.nt, it.Lk);
+#pragma unroll
+    for (int j = 0; j < kWin / kPrefillThreads; ++j) {
+      const int i = j * kPrefillThreads + w * kWave + lane;
+      __builtin_amdgcn_global_load_lds(row + (i < nblk ? i : nblk - 1),
+                                       &win[wi * kWin + j * kPrefillThreads + w * kWave], 4, 0, 0);
+    }
+  };
+
+  // ---- rounds of the current item X, the next (Y) and the one after (Z), -1
+  // when absent; the fields of X and Y the steps read; windows by item count
+  int kx = find_item(0);
+  if (kx < 0) return;
+  int ky = find_item(kx + 1);
+  int kz = ky < 0 ? -1 : find_item(ky + 1);
+  int x_hk, x_lk, x_nt, y_hk = 0, y_lk = 0, y_nt = 0;
+  int nitem = 0;                // items begun; X's window is nitem % 3
+  int wbase = 0;                // first block id in X's window
+  int kt = 0;                   // X's tile at this step
+  auto win_of = [&](int ahead) __attribute__((always_inline)) { return (nitem + ahead) % 3; };
+  // per item, so that a step does no division: X's and Y's windows (offsets
+  // into win; indexed from win itself, so that the compiler sees these reads
+  // never touch the K/V buffers that copies in flight write) and KV-head
+  // offsets in the pool (16-byte units)
+  int x_win = 0, y_win = kWin;
+  int x_hoff = 0, y_hoff = 0;
+  int dma_k = -1;               // round whose window is to be loaded in the next step
+  // a window's ids in flight: loaded into registers in one step, written to LDS
+  // at the start of the next (or at an item switch); plain stores, so that the
+  // compiler sees exactly which LDS they write (an LDS copy in flight into the
+  // windows would make every fragment read of the step wait for it)
+  int idv[kWin / kPrefillThreads];
+  int idv_dst = -1;
+
+  // per-lane and per-wave state of X
+  int lim, wave_last, wave_lim_min;
+  uint4 qf[kKS];
+  f32x16_t o[kDB];
+  float m, lsum;
+  // make the item of round k current: its fields, this lane's mask limit, Q rows
+  auto begin_item = [&](int k) __attribute__((always_inline)) {
+    const Item it = item_info(int(rank_at(k)));
+    x_hk = it.hk;
+    x_lk = it.Lk;
+    x_nt = it.nt;
+    x_hoff = it.hk * slab16;
+    x_win = win_of(0) * kWin;
+    y_win = win_of(1) * kWin;
+    const int qrow = it.row0 + col % kBM;
+    const int last = it.Lk - it.Lq + qrow;
+    lim = last < it.Lk - 1 ? last : it.Lk - 1;
+    const int rr = qrow < it.Lq - 1 ? qrow : it.Lq - 1;   // rows past Lq are not written
+    const int needed = it.Lk - it.Lq + rr < it.Lk - 1 ? it.Lk - it.Lq + rr : it.Lk - 1;
+    wave_last = __builtin_amdgcn_readfirstlane(int(wave_max(float(needed))));
+    wave_lim_min = __builtin_amdgcn_readfirstlane(int(-wave_max(-float(lim))));
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        a.q + ((long long)(it.q0 + rr) * a.num_q_heads + it.hk * kG + col / kBM) * kD);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) qf[ks] = qp[ks * 2 + half];
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  };
+  auto next_fields = [&]() __attribute__((always_inline)) {
+    if (ky >= 0) {
+      const Item it = item_info(int(rank_at(ky)));
+      y_hk = it.hk;
+      y_lk = it.Lk;
+      y_nt = it.nt;
+      y_hoff = it.hk * slab16;
+    }
+  };
+
+  auto window_load = [&](int k, int wi) __attribute__((always_inline)) {
+    const Item it = item_info(int(rank_at(k)));
+    const int* row = a.block_tables + (long long)it.s * a.max_blocks_per_seq;
+    const int nblk = item_blocks(it.nt, it.Lk);
+#pragma unroll
+    for (int j = 0; j < kWin / kPrefillThreads; ++j) {
+      const int i = j * kPrefillThreads + tid;
+      idv[j] = row[i < nblk ? i : nblk - 1];
+    }
+    idv_dst = wi * kWin;
+  };
+  auto window_store = [&]() __attribute__((always_inline)) {
+    if (idv_dst >= 0) {
+#pragma unroll
+      for (int j = 0; j < kWin / kPrefillThreads; ++j) win[idv_dst + j * kPrefillThreads + tid] = idv[j];
+      idv_dst = -1;
+    }
+  };
+
+  // ---- copies: the pool's rows straight into LDS (global_load_lds, 16 bytes
+  // per lane); with blocks of at least one tile a tile lies in one block, keys
+  // past Lk read slots of that block (in bounds; masked, their V zeroed).
+  // Offsets (16-byte units) of tile t of KV head hk inside a block: K rows, V rows
+  auto k_off = [&](int hoff, int t) __attribute__((always_inline)) { return hoff + ((t * kBN) & bmask); };
+  auto v_off = [&](int hoff, int t) __attribute__((always_inline)) { return hoff + (((t * kBN) & bmask) >> 3) * kD; };
+  auto issue_k = [&](int off, int blk, uint4 (*ks)[kBN]) __attribute__((always_inline)) {
+    const uint4* ksrc = kbase + ((long long)blk * blk16 + off) + lane;
+#pragma unroll
+    for (int u = 0; u < kKW; ++u) {
+      const int c = w * kKW + u;
+      load_row_to_lds(ksrc + (c << bshift), &ks[c][0]);
+    }
+  };
+  auto issue_v = [&](int off, int blk, uint4 (*vs)[kD]) __attribute__((always_inline)) {
+    const uint4* vb = vbase + ((long long)blk * blk16 + off) + lane;
+#pragma unroll
+    for (int u = 0; u < kVW; ++u) {
+      const int e = w * kVW + u;
+      const int j = e / (kD / 64), dh = e % (kD / 64);
+      load_row_to_lds(vb + j * kD + dh * 64, &vs[j][dh * 64]);
+    }
+  };
+  // once a V tile with `valid` keys before the end of its item's context has
+  // landed in vs (after a barrier), zero the V values of the keys past it: their
+  // weights are 0, but a stale or NaN value would still poison 0 * v
+  auto fix_tail = [&](int valid, uint4 (*vs)[kD]) __attribute__((always_inline)) {
+    if (valid >= kBN) return;
+    for (int e = tid; e < (kBN / 8) * kD; e += kPrefillThreads) {
+      const int j = e / kD, d = e % kD;
+      const int nv = valid - j * 8;
+      if (nv < 8) {
+        uint4 v = vs[j][d];
+        v.x &= (0 < nv ? 0x0000ffffu : 0u) | (1 < nv ? 0xffff0000u : 0u);
+        v.y &= (2 < nv ? 0x0000ffffu : 0u) | (3 < nv ? 0xffff0000u : 0u);
+        v.z &= (4 < nv ? 0x0000ffffu : 0u) | (5 < nv ? 0xffff0000u : 0u);
+        v.w &= (6 < nv ? 0x0000ffffu : 0u) | (7 < nv ? 0xffff0000u : 0u);
+        vs[j][d] = v;
+      }
+    }
+    __syncthreads();
+  };
+  // move X's window so that it starts at block `first` (every thread; between
+  // barriers; only for items longer than a window)
+  auto refill = [&](int first) __attribute__((always_inline)) {
+    __syncthreads();
+    const Item it = item_info(int(rank_at(kx)));
+    const int* row = a.block_tables + (long long)it.s * a.max_blocks_per_seq;
+    const int nblk = item_blocks(it.nt, it.Lk);
+    const int xw = win_of(0) * kWin;
+    for (int i = tid; i < kWin && first + i < nblk; i += kPrefillThreads) win[xw + i] = row[first + i];
+    wbase = first;
+    __syncthreads();
+  };
+
+  // ---- the copies of a step, planned one step ahead: the offset of the tile
+  // inside its block (-1: no copy) and the block id, read from LDS then and kept
+  // raw in a VGPR so that the read's latency is not waited for. cv_valid: keys
+  // of the V tile before the end of its item's context.
+  int ck_off, cv_off, cv_valid;
+  int ck_id, cv_id;
+  // plan the step at X's tile t0 (Y follows when ky >= 0). Common case: both
+  // copies read X (one branch); the last two steps of an item also read Y.
+  auto plan = [&](int t0) __attribute__((always_inline)) {
+    const int tk = t0 + 2, tv = t0 + 1, n = x_nt;
+    const int bk = (tk * kBN) >> bshift, bv = (tv * kBN) >> bshift;
+    if (__builtin_expect(tk < n, 1)) {
+      if (__builtin_expect(bk - wbase >= kWin, 0)) refill(bv);
+      ck_off = k_off(x_hoff, tk);
+      ck_id = win[x_win + bk - wbase];
+      cv_off = v_off(x_hoff, tv);
+      cv_valid = x_lk - tv * kBN;
+      cv_id = win[x_win + bv - wbase];
+      return;
+    }
+    ck_off = cv_off = -1;
+    cv_valid = kBN;
+    if (ky >= 0 && tk == n) {
+      ck_off = k_off(y_hoff, 0);
+      ck_id = win[y_win];
+    } else if (ky >= 0 && tk == n + 1 && y_nt >= 2) {
+      ck_off = k_off(y_hoff, 1);
+      ck_id = win[y_win + (kBN >> bshift)];
+    }
+    if (tv < n) {
+      cv_off = v_off(x_hoff, tv);
+      cv_valid = x_lk - tv * kBN;
+      cv_id = win[x_win + bv - wbase];
+    } else if (ky >= 0) {
+      cv_off = v_off(y_hoff, 0);
+      cv_valid = y_lk;
+      cv_id = win[y_win];
+    }
+  };
+
+  // ---- the tile arithmetic (as in the one-item kernel)
+  auto qk_tile = [&](const uint4 (*kc)[kBN], f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kc[ks * 2 + half][mb * 32 + l32]),
+                                                           as_bf16x8(qf[ks]), sacc[mb], 0, 0, 0);
+  };
+  auto softmax_max = [&](f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+    const int key0 = kt * kBN;
+    if (key0 + kBN - 1 > wave_lim_min) {   // some column masks keys here
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+          if (key > lim) sacc[mb][i] = -INFINITY;
+        }
+    }
+    float smax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) smax = max3f(smax, sacc[mb][i], sacc[mb][i + 1]);
+    smax = pair_max(smax);
+    const float mt = smax * sc;
+    const bool grow = mt > m + 8.f;
+    if (__any(grow)) {
+      const float mn = grow ? mt : m;
+      const float alpha = grow ? fast_exp2(m - mn) : 1.f;   // m = -inf: no key seen yet
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m = mn;
+    }
+  };
+  uint4 pf[4];
+  auto softmax_exp = [&](f32x16_t (&sacc)[2]) __attribute__((always_inline)) {
+    const float mneg = m == -INFINITY ? 0.f : -m;
+    uint32_t packed[2][8];
+    float ps = lsum;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        f32x2_t pp;
+        pp.x = fast_exp2(fmaf(sacc[mb][i], sc, mneg));
+        pp.y = fast_exp2(fmaf(sacc[mb][i + 1], sc, mneg));
+        const bf16x2_t pk = __builtin_convertvector(pp, bf16x2_t);
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pk, kOnesBf16x2, ps, false);
+        packed[mb][i / 2] = __builtin_bit_cast(uint32_t, pk);
+      }
+    lsum = ps;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const auto r0 = __builtin_amdgcn_permlane32_swap(packed[mb][4 * j], packed[mb][4 * j + 2], false, false);
+        const auto r1 = __builtin_amdgcn_permlane32_swap(packed[mb][4 * j + 1], packed[mb][4 * j + 3], false, false);
+        pf[2 * mb + j] = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+      }
+  };
+  auto pv_tile = [&](const uint4 (*vc)[kD]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vc[2 * t + half][db * 32 + l32]),
+                                                        as_bf16x8(pf[t]), o[db], 0, 0, 0);
+  };
+  // normalise and write X's rows of this lane
+  auto write_out = [&]() __attribute__((always_inline)) {
+    uint16_t* op = out_row(item_info(int(rank_at(kx))));
+    const float L = pair_sum(lsum);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (op) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + half * 4;
+          const f32x2_t lo = {o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv};
+          const f32x2_t hi = {o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv};
+          *reinterpret_cast<uint2*>(op + d) =
+              make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t)));
+        }
+    }
+  };
+
+  // ---- one step at X's tile kt: copies planned by the previous step; the
+  // softmax and PV of tile kt with the QK^T of tile kt+1 interleaved (on X's
+  // last tile that QK^T reads whatever K buffer is there and its scores are
+  // dropped: one code path for every step keeps the registers of the
+  // one-item kernel). After the barrier of X's last step: X's output, then Y
+  // becomes X, its Q rows are loaded and its first QK^T runs.
+  // Returns false when the workgroup has no item left.
+  f32x16_t s_a[2], s_b[2];
+  auto step = [&](const uint4 (*k_next)[kBN], const uint4 (*v_cur)[kD], uint4 (*k_dst)[kBN],
+                  uint4 (*v_dst)[kD], uint4 (*k_alt)[kBN], f32x16_t (&s_cur)[2], f32x16_t (&s_next)[2]) __attribute__((always_inline)) {
+    // this step's copies (planned by the previous step); the next step's are
+    // planned first, while no copy is in flight, so that the window reads wait
+    // for nothing
+    const int koff = ck_off, voff = cv_off, tail_valid = cv_off >= 0 ? cv_valid : kBN;
+    const int kid = __builtin_amdgcn_readfirstlane(ck_id), vid = __builtin_amdgcn_readfirstlane(cv_id);
+    const bool last = kt + 1 == x_nt;
+    window_store();
+    if (__builtin_expect(!last, 1)) plan(kt + 1);
+    if (__builtin_expect(koff >= 0, 1)) issue_k(koff, kid, k_dst);
+    if (__builtin_expect(voff >= 0, 1)) issue_v(voff, vid, v_dst);
+    // the window of the item after next: its ids land by this step's barrier
+    if (__builtin_expect(dma_k >= 0, 0)) {
+      window_load(dma_k, win_of(2));
+      dma_k = -1;
+    }
+    if (__builtin_expect(kt * kBN <= wave_last, 1)) {
+      softmax_max(s_cur);
+      // the two waves sharing a SIMD come from different workgroups; while this
+      // one issues MFMAs it takes issue priority, so that the matrix pipe stays
+      // fed when both are ready
+      __builtin_amdgcn_s_setprio(1);
+      qk_tile(k_next, s_next);
+      softmax_exp(s_cur);
+      constexpr int kQkMfma = 2 * kKS, kQkReads = 2 * kKS, kLead = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kQkMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 96 / kQkMfma, 0);
+        if (i < kQkReads - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      pv_tile(v_cur);
+      constexpr int kPvReads = 4 * kDB;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+      for (int i = 0; i < kPvReads - kLead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();
+    if (__builtin_expect(tail_valid < kBN, 0)) fix_tail(tail_valid, v_dst);
+    if (__builtin_expect(!last, 1)) {
+      ++kt;
+      return true;
+    }
+    write_out();
+    if (ky < 0) return false;
+    // Y becomes X, Z becomes Y; the window X used takes the item after Z
+    const bool one_tile = x_nt == 1;
+    kx = ky;
+    ky = kz;
+    kz = kz < 0 ? -1 : find_item(kz + 1);
+    ++nitem;
+    wbase = 0;
+    kt = 0;
+    begin_item(kx);
+    next_fields();
+    window_store();
+    // after a one-tile item no step has copied this item's first K tile yet
+    if (one_tile) issue_k(k_off(x_hoff, 0), __builtin_amdgcn_readfirstlane(win[x_win]), k_alt);
+    // each wave copies a quarter of a tile's rows and writes part of a window:
+    // all wait for all
+    __syncthreads();
+    plan(0);
+    dma_k = kz;                    // copied by the next step
+    if (0 <= wave_last) qk_tile(k_next, s_next);   // K of X's first tile sits in k_next
+    __syncthreads();               // every wave is done with that K before it is copied over
+    return true;
+  };
+
+  // ---- first item: windows of X and Y, then X's first tiles and Q rows
+  window_dma(kx, win_of(0));
+  if (ky >= 0) window_dma(ky, win_of(1));
+  __syncthreads();
+  begin_item(kx);
+  next_fields();
+  plan(0);
+  issue_k(k_off(x_hoff, 0), __builtin_amdgcn_readfirstlane(win[x_win]), k_a);
+  issue_v(v_off(x_hoff, 0), __builtin_amdgcn_readfirstlane(win[x_win]), v_a);
+  if (x_nt >= 2) issue_k(k_off(x_hoff, 1), __builtin_amdgcn_readfirstlane(win[x_win + (kBN >> bshift)]), k_b);
+  dma_k = kz;                      // copied by the first step
+  __syncthreads();
+  fix_tail(x_lk, v_a);
+  if (0 <= wave_last) qk_tile(k_a, s_a);
+  __syncthreads();
+  // position parity picks the buffers: K(p) in k_a / k_b and V(p) in v_a / v_b
+  // by p mod 2, p counting tiles over the workgroup's items
+  for (;;) {
+    if (!step(k_b, v_a, k_a, v_b, k_b, s_a, s_b)) break;
+    if (!step(k_a, v_b, k_b, v_a, k_a, s_b, s_a)) break;
+  }
+}
+
 constexpr int kNBLaunch = PA_PREFILL_NB;
 
 template <int kD, bool kFp8, bool kBig, bool kPacked = false>
@@ -769,6 +1302,37 @@ static bool launch_prefill_g(int G, const PrefillArgs& a, unsigned grid, hipStre
   if (!a.block_tables) return !kFp8 && launch_prefill_gb<kD, false, false, true>(G, a, grid, stream);
   return a.block_size >= kBN ? launch_prefill_gb<kD, kFp8, true>(G, a, grid, stream)
                              : launch_prefill_gb<kD, kFp8, false>(G, a, grid, stream);
+}
+
+template <int kD>
+static bool launch_prefill_persist(int G, const PrefillArgs& a, int num_items, unsigned grid, hipStream_t stream) {
+  switch (G) {
+    case 1: prefill_persist_kernel<kD, 1><<<grid, kPrefillThreads, 0, stream>>>(a, num_items); return true;
+    case 2: prefill_persist_kernel<kD, 2><<<grid, kPrefillThreads, 0, stream>>>(a, num_items); return true;
+    case 4: prefill_persist_kernel<kD, 4><<<grid, kPrefillThreads, 0, stream>>>(a, num_items); return true;
+    case 8: prefill_persist_kernel<kD, 8><<<grid, kPrefillThreads, 0, stream>>>(a, num_items); return true;
+    default: return false;
+  }
+}
+
+// resident workgroups of a persistent prefill launch: 0 = two per CU (what the
+// kernel's registers and LDS allow), > 0 = that many, < 0 = no persistent
+// launch (one workgroup per work item)
+static int g_prefill_slots = 0;
+
+void set_prefill_slots(int n) { g_prefill_slots = n; }
+
+// compute units of the current device (looked up once per device)
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
@@ -799,9 +1363,22 @@ hipError_t launch_prefill(const uint16_t* q, const uint8_t* k_cache, const uint8
   a.cap_k = max_seqlen_k;
   a.num_qblocks = (max_seqlen_q + bm - 1) / bm;
   a.scale_log2 = scale * kLog2e;
-  const unsigned grid = unsigned((long long)num_seqs * a.num_qblocks * pool.num_kv_heads);
+  const long long items = (long long)num_seqs * a.num_qblocks * pool.num_kv_heads;
+  const unsigned grid = unsigned(items);
   if (grid == 0) return hipSuccess;
   bool ok;
+  // bf16 pool, blocks of at least one tile: the persistent kernel
+  if (kNBLaunch == 1 && block_tables && !pool.fp8 && pool.block_size >= kBN && num_seqs <= kSortMax &&
+      g_prefill_slots >= 0 && items <= 0x7fffffffLL) {
+    const int slots = g_prefill_slots > 0 ? g_prefill_slots : 2 * device_cus();
+    if (slots > 0) {
+      const unsigned pg = items < slots ? unsigned(items) : unsigned(slots);
+      ok = pool.head_dim == 64 ? launch_prefill_persist<64>(G, a, int(items), pg, stream)
+                               : launch_prefill_persist<128>(G, a, int(items), pg, stream);
+      if (!ok) return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+  }
   if (pool.head_dim == 64)
     ok = pool.fp8 ? launch_prefill_g<64, true>(G, a, grid, stream) : launch_prefill_g<64, false>(G, a, grid, stream);
   else
