@@ -114,3 +114,35 @@ def test_persistent_long_context_window_refill(set_slots):
     w = W.custom(seed=350, Hq=8, Hkv=2, D=128, bs=64, context_lens=(),
                  prefill=[(20000, 40), (17000, 100), (100, 30), (16380, 9)])
     _check_all_slots(w, set_slots, slots=(0, 1, 3))
+
+
+def test_persistent_random_shapes(set_slots):
+    """Seeded random batches (head groupings, head sizes, block sizes, prefix and
+    chunk lengths, now and then fewer keys than queries): the persistent launch
+    at several resident-workgroup counts equals one workgroup per item bit for
+    bit; the oracle checks one batch in four."""
+    rng = np.random.default_rng(351)
+    for trial in range(24):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        bs = int(rng.choice([64, 128, 256]))
+        nseq = int(rng.integers(1, 13))
+        pf = [(int(rng.integers(0, 700)), int(rng.integers(1, 260))) for _ in range(nseq)]
+        w = W.custom(seed=352 + trial, Hq=hkv * g, Hkv=hkv, D=d, bs=bs, context_lens=(), prefill=pf)
+        if rng.random() < 0.3:
+            lk = np.diff(w.cu_seqlens_k).astype(np.int64)
+            i = int(rng.integers(0, nseq))
+            lk[i] = int(rng.integers(0, lk[i] + 1))
+            w.cu_seqlens_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        print(f"trial {trial}: G={g} Hkv={hkv} D={d} bs={bs} chunks={pf} lk={np.diff(w.cu_seqlens_k).tolist()}",
+              flush=True)
+        case = GpuCase(w)
+        set_slots(-1)
+        ref = host_bits(case.prefill())
+        for n in (0, 1, 3, 7):
+            set_slots(n)
+            got = host_bits(case.prefill())
+            assert np.array_equal(got, ref), f"trial {trial}, slots={n}"
+        if trial % 4 == 0:
+            assert_close(bf16_f64(ref), _oracle(w), *TOL, what=f"trial {trial}")
