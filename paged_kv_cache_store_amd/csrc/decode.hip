@@ -15,14 +15,17 @@
 // * a wave takes 64-key tiles of the partition in turn (tile t -> wave t % 4);
 // * QK: lane = key. The K layout keeps 8 (bf16) or 16 (fp8) head-dim values of
 //   one key in 16 bytes and consecutive keys in consecutive 16-byte slots, so a
-//   wave's load of chunk c covers 1 KiB contiguous; the lane forms the whole dot
-//   product for its key with v_dot2_f32_bf16 against wave-uniform query pairs,
-//   with no cross-lane reduction;
+//   wave's load of chunk c covers 1 KiB contiguous; the lane's scores of its key
+//   for the G query heads come out of v_mfma_f32_4x4x4_16b_bf16 blocks that take
+//   its own K registers as they were loaded (the query rows from LDS), with no
+//   cross-lane reduction;
 // * softmax: per tile, a DPP wave maximum per query head, running max/sum with
 //   rescaling (base-2 exponentials, log2(e) folded into the scale);
 // * PV: lane = head-dim index. The V layout keeps 8 (bf16) or 16 (fp8)
-//   consecutive keys of one head-dim index in 16 bytes, so a lane dots its V
-//   chunk with the chunk's bf16 weights (broadcast from LDS) via v_dot2;
+//   consecutive keys of one head-dim index in 16 bytes; the same 4x4x4 blocks
+//   take a lane's V registers as loaded against the tile's bf16 weights (from
+//   LDS). (PA_DECODE_MFMA=0 builds the earlier form: v_dot2_f32_bf16 against
+//   wave-uniform query pairs and broadcast weights.)
 // * the 4 waves' partial (max, sum, output) are merged in LDS; a sequence that
 //   fits one partition writes its bf16 output, a longer one writes an
 //   unnormalised float32 partial for the reduce kernel.
@@ -48,6 +51,14 @@ namespace pa {
 #ifndef PA_DECODE_ORDER_MIN_CONTEXT
 #define PA_DECODE_ORDER_MIN_CONTEXT 1024
 #endif
+
+// Q.K^T and P.V on the matrix cores (4x4x4 blocks); 0: on the VALU (v_dot2)
+#ifndef PA_DECODE_MFMA
+#define PA_DECODE_MFMA 1
+#endif
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDecodeThreads = PA_DECODE_WAVES * 64;
 constexpr int kDecodeWaves = kDecodeThreads / kWave;
@@ -138,10 +149,12 @@ __device__ __forceinline__ void stage_new_token(const DecodeArgs& a, uint4 x, in
 // Waves per SIMD the compiler must leave room for. The variants that take the
 // newest token from the caller need a few more registers than the plain ones
 // and would drop to 2 waves; held at 3 they do not spill (fp8 with one query
-// head per KV head would).
+// head per KV head would). The plain fp8 ones with G <= 4 fit 4 waves; left
+// free, the compiler moves their accumulators to AGPRs and runs 3.
 constexpr int decode_min_waves(int g, bool fp8, bool with_new) {
   return PA_DECODE_WAVES_PER_EU ? PA_DECODE_WAVES_PER_EU
-                                : (with_new && g < 8 && !(fp8 && g == 1) ? 3 : 1);
+         : fp8 && !with_new && g <= 4 && PA_DECODE_MFMA ? 4
+         : (with_new && g < 8 && !(fp8 && g == 1) ? 3 : 1);
 }
 
 // kNew: sequence s's position context_lens[s]-1 is read from new_k / new_v
@@ -156,12 +169,31 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int kDL = kD / kWave;         // head-dim values per lane in PV
   constexpr int kQW = kD / 2;             // query dwords (bf16 pairs) per head
   constexpr int kPW = kX / 2;             // weight dwords per V key-chunk
+  // kVM: both products on v_mfma_f32_4x4x4_16b_bf16 (16
+  // independent 4x4x4 blocks per instruction; in block b = lane/4, lane l
+  // holds row l%4 of A, column l%4 of B and of the result), with the K and V
+  // registers used as loaded.
+  // * S = Q K^T, four head-dims per step: rows = the query heads, columns =
+  //   the block's four keys. Lane l's B operand is its own key's K at those
+  //   head-dims, its A operand head l%4's query there (from LDS), and its
+  //   result the scores of its key for heads 0..3, the layout of the VALU form.
+  // * O^T += V^T P^T, four keys per step: rows = head-dims 4b..4b+3 (+ 64 dl),
+  //   columns = the query heads. Lane l's A operand is its own head-dim's V at
+  //   those keys, its B operand head l%4's weights there, and its accumulator
+  //   holds head l%4 at head-dims 4*(l/4)..+3.
+  // The query heads go four to a set of rows/columns (G = 8: two sets); with
+  // G < 4 the padding rows/columns repeat the last head and are never read.
+  constexpr bool kVM = PA_DECODE_MFMA;
+  constexpr int kHS = kG > 4 ? kG / 4 : 1;   // sets of four query heads
+  constexpr int kKStep = kX / 4;             // 4x4x4 steps per 16-byte K chunk or V unit
 
   __shared__ int blk_s[kMaxPartBlocks];
   __shared__ __attribute__((aligned(16))) uint16_t p_s[kDecodeWaves][kG][kTile];
   __shared__ float m_s[kDecodeWaves][kG];
   __shared__ float l_s[kDecodeWaves][kG];
   __shared__ float o_s[kDecodeWaves][kG][kD];
+  // kVM: the G query heads of this KV head (bf16), the A operands of S = Q K^T
+  __shared__ __attribute__((aligned(16))) uint16_t q_s[kVM ? kG : 1][kVM ? kD : 8];
 
   const int Hkv = a.num_kv_heads;
   const int bid = blockIdx.x;
@@ -205,7 +237,22 @@ void decode_kernel(const DecodeArgs a) {
   // physical block ids of this partition
   const int nb = (pend - p0 + bs - 1) / bs;
   const int* bt = a.block_tables + (long long)s * a.max_blocks_per_seq + p0 / bs;
+  // kVM: wave 0 stages the query heads in LDS, its load beside the table's
+  constexpr int kQ16 = kG * kD / 8;   // 16-byte pieces of the G query rows
+  constexpr int kQL = (kQ16 + kWave - 1) / kWave;
+  static_assert(kQL <= 2 && (kQ16 % kWave == 0 || kQL == 1), "query staging");
+  uint4 qv0 = make_uint4(0, 0, 0, 0), qv1 = qv0;
+  const bool qload = kVM && w == 0 && (kQ16 % kWave == 0 || lane < kQ16 % kWave);
+  if (qload) {
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD);
+    qv0 = qsrc[lane];
+    if (kQL > 1) qv1 = qsrc[lane + kWave];
+  }
   for (int i = tid; i < nb; i += kDecodeThreads) blk_s[i] = bt[i];
+  if (qload) {
+    reinterpret_cast<uint4*>(&q_s[0][0])[lane] = qv0;
+    if (kQL > 1) reinterpret_cast<uint4*>(&q_s[0][0])[lane + kWave] = qv1;
+  }
   if (kNew && slot_new >= 0) stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
   // (the barrier that publishes blk_s and tok_s comes after the first tile's
   // loads are issued, below)
@@ -218,14 +265,22 @@ void decode_kernel(const DecodeArgs a) {
   const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache) + (long long)h * slab16;
   const long long blk_stride16 = (long long)Hkv * slab16;
 
-  float m[kG], l[kG], acc[kG][kDL];
+  float m[kG], l[kG], acc[kVM ? 1 : kG][kDL];
+  f32x4_t acc4[kHS][kDL];
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kDL; ++j) acc[g][j] = 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < kDL; ++j) {
+#pragma unroll
+    for (int g = 0; g < (kVM ? 1 : kG); ++g) acc[g][j] = 0.f;
+#pragma unroll
+    for (int hs = 0; hs < kHS; ++hs) acc4[hs][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int hcol = lane & 3;   // kVM: this lane's query head in the 4x4 blocks (of each set)
+  auto head_of = [&](int hs) { return hs * 4 + hcol < kG ? hs * 4 + hcol : kG - 1; };
 
   const int ntiles = (pend - p0 + kTile - 1) / kTile;
 
@@ -265,7 +320,44 @@ void decode_kernel(const DecodeArgs a) {
     float sv[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) sv[g] = 0.f;
-    if constexpr (kG >= 2) {
+    if constexpr (kVM) {
+      f32x4_t sacc[kHS];
+#pragma unroll
+      for (int hs = 0; hs < kHS; ++hs) sacc[hs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kKC; ++c) {
+        const uint32_t kw[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+        uint32_t kb[2 * kKStep];   // the chunk's kX head-dims as bf16 pairs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kFp8) {
+            kb[2 * i] = fp8x2_to_bf16x2<false>(kw[i]);
+            kb[2 * i + 1] = fp8x2_to_bf16x2<true>(kw[i]);
+          } else {
+            kb[i] = kw[i];
+          }
+        }
+#pragma unroll
+        for (int hs = 0; hs < kHS; ++hs) {
+          const uint4* qrow = reinterpret_cast<const uint4*>(&q_s[head_of(hs)][c * kX]);
+          uint32_t qw[2 * kKStep];
+#pragma unroll
+          for (int u = 0; u < kKStep / 2; ++u) {
+            const uint4 q4 = qrow[u];
+            qw[4 * u] = q4.x; qw[4 * u + 1] = q4.y; qw[4 * u + 2] = q4.z; qw[4 * u + 3] = q4.w;
+          }
+#pragma unroll
+          for (int i = 0; i < kKStep; ++i) {   // head-dims kX*c + 4i .. +3
+            const uint2 av = make_uint2(qw[2 * i], qw[2 * i + 1]);
+            const uint2 bv = make_uint2(kb[2 * i], kb[2 * i + 1]);
+            sacc[hs] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_t, av),
+                                                             __builtin_bit_cast(bf16x4_t, bv), sacc[hs], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < kG; ++g) sv[g] = sacc[g / 4][g % 4];
+    } else if constexpr (kG >= 2) {
       // One query head at a time. The G heads' 64*G query dwords do not fit in
       // a wave's SGPRs; held for the whole loop they are spilled to VGPR lanes
       // and read back every tile (one v_readlane each). Here a head's dwords
@@ -316,6 +408,9 @@ void decode_kernel(const DecodeArgs a) {
       }
     }
     // ---- online softmax (base 2)
+    float alpha_col[kHS];   // kVM: the factor of this lane's column (of each set)
+#pragma unroll
+    for (int hs = 0; hs < kHS; ++hs) alpha_col[hs] = 1.f;
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
       const float x = valid ? sv[g] * sc : -INFINITY;
@@ -323,10 +418,20 @@ void decode_kernel(const DecodeArgs a) {
       const float alpha = fast_exp2(m[g] - mn);
       const uint32_t pb = f32_to_bf16(fast_exp2(x - mn));
       l[g] = l[g] * alpha + bf16_lo(pb);
+      if constexpr (kVM) {
+        alpha_col[g / 4] = hcol == g % 4 ? alpha : alpha_col[g / 4];
+      } else {
 #pragma unroll
-      for (int dl = 0; dl < kDL; ++dl) acc[g][dl] *= alpha;
+        for (int dl = 0; dl < kDL; ++dl) acc[g][dl] *= alpha;
+      }
       m[g] = mn;
       p_s[w][g][lane] = uint16_t(pb);
+    }
+    if constexpr (kVM) {
+#pragma unroll
+      for (int hs = 0; hs < kHS; ++hs)
+#pragma unroll
+        for (int dl = 0; dl < kDL; ++dl) acc4[hs][dl] *= alpha_col[hs];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -339,6 +444,59 @@ void decode_kernel(const DecodeArgs a) {
       const int kk = key0 + j * kX;
       if (kk >= pend) break;
       const int nv = pend - kk;
+      if constexpr (kVM) {
+        // the chunk's kX keys of each head-dim this lane holds, as bf16 pairs
+        // (the values past the context's end zeroed: their weights are 0, but
+        // a NaN would poison 0 * v)
+        uint32_t vb[kDL][2 * kKStep];
+#pragma unroll
+        for (int dl = 0; dl < kDL; ++dl) {
+          uint32_t vw[4] = {vr[j][dl].x, vr[j][dl].y, vr[j][dl].z, vr[j][dl].w};
+          if (nv < kX) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              uint32_t mask = 0;
+              if constexpr (!kFp8) {
+                mask = (2 * i < nv ? 0x0000ffffu : 0u) | (2 * i + 1 < nv ? 0xffff0000u : 0u);
+              } else {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) mask |= (4 * i + b < nv) ? (0xffu << (8 * b)) : 0u;
+              }
+              vw[i] &= mask;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (kFp8) {
+              vb[dl][2 * i] = fp8x2_to_bf16x2<false>(vw[i]);
+              vb[dl][2 * i + 1] = fp8x2_to_bf16x2<true>(vw[i]);
+            } else {
+              vb[dl][i] = vw[i];
+            }
+          }
+        }
+#pragma unroll
+        for (int hs = 0; hs < kHS; ++hs) {
+          // head head_of(hs)'s weights of the chunk's keys (B operands, four keys each)
+          const uint4* pp = reinterpret_cast<const uint4*>(&p_s[w][head_of(hs)][j * kX]);
+          uint32_t pq[2 * kKStep];
+#pragma unroll
+          for (int u = 0; u < kKStep / 2; ++u) {
+            const uint4 p4 = pp[u];
+            pq[4 * u] = p4.x; pq[4 * u + 1] = p4.y; pq[4 * u + 2] = p4.z; pq[4 * u + 3] = p4.w;
+          }
+#pragma unroll
+          for (int dl = 0; dl < kDL; ++dl)
+#pragma unroll
+            for (int i = 0; i < kKStep; ++i) {
+              const uint2 av = make_uint2(vb[dl][2 * i], vb[dl][2 * i + 1]);
+              const uint2 bv = make_uint2(pq[2 * i], pq[2 * i + 1]);
+              acc4[hs][dl] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                  __builtin_bit_cast(bf16x4_t, av), __builtin_bit_cast(bf16x4_t, bv), acc4[hs][dl], 0, 0, 0);
+            }
+        }
+        continue;
+      }
       uint32_t pw[kG][kPW];
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -486,8 +644,21 @@ void decode_kernel(const DecodeArgs a) {
       m_s[w][g] = m[g];
       l_s[w][g] = lw;
     }
+    if constexpr (!kVM) {
 #pragma unroll
-    for (int dl = 0; dl < kDL; ++dl) o_s[w][g][lane + dl * kWave] = acc[g][dl];
+      for (int dl = 0; dl < kDL; ++dl) o_s[w][g][lane + dl * kWave] = acc[g][dl];
+    }
+  }
+  if constexpr (kVM) {
+#pragma unroll
+    for (int hs = 0; hs < kHS; ++hs) {
+      if (hs * 4 + hcol < kG) {
+#pragma unroll
+        for (int dl = 0; dl < kDL; ++dl)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o_s[w][hs * 4 + hcol][dl * kWave + (lane & ~3) + i] = acc4[hs][dl][i];
+      }
+    }
   }
   __syncthreads();
   const float vsc = kFp8 ? as_constant(a.v_scale)[h] : 1.f;
