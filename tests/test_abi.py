@@ -196,3 +196,21 @@ def test_alignment_rules(lib):
     assert store_decode(lib, desc(), sm=odd4) == UNSUP
     assert prefill(lib, desc(), q=odd16) == UNSUP
     assert lib.pa_copy_blocks(odd16, FAKE, FAKE, 1, ctypes.byref(desc()), None) == UNSUP
+
+
+def test_decode_vector_alu_form_compiles(tmp_path):
+    """The decode kernel's other form (PA_DECODE_MFMA=0: the products on the
+    VALU with v_dot2) still compiles for gfx950 (device code only)."""
+    import os
+    import shutil
+    import subprocess
+
+    import paged_kv_cache_store_amd.build as B
+    if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path / "decode_valu.o"
+    cmd = [B.HIPCC, *B.DEVICE_FLAGS, "-DPA_DECODE_MFMA=0", "--cuda-device-only", "-I", B.INCLUDE, "-I", B.CSRC,
+           "-c", os.path.join(B.CSRC, "decode.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert out.stat().st_size > 0
