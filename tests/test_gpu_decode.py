@@ -53,13 +53,18 @@ EDGE = [
     dict(seed=107, Hq=8, Hkv=4, D=64, bs=16, context_lens=(1, 16, 17, 100), kv_dtype="fp8"),
     dict(seed=108, Hq=8, Hkv=1, D=64, bs=64, context_lens=(2000, 3), kv_dtype="fp8", partition_size=256),
     dict(seed=109, Hq=4, Hkv=4, D=128, bs=16, context_lens=(4096, 1, 77), partition_size=512),
-    # every (G, D, dtype) the decode kernels are built for, both QK^T loop orders
+    # with the cases above, every (G, D, dtype) the decode kernels are built for
+    # (G 1/2/4/8: one set of 4x4x4 MFMA columns with padding, or two sets)
     dict(seed=110, Hq=16, Hkv=2, D=128, bs=32, context_lens=(3, 64, 65, 450), kv_dtype="fp8"),
     dict(seed=111, Hq=4, Hkv=4, D=128, bs=64, context_lens=(1, 129, 700), kv_dtype="fp8"),
     dict(seed=112, Hq=16, Hkv=4, D=64, bs=256, context_lens=(2, 255, 600), kv_dtype="fp8",
          partition_size=256),
     dict(seed=113, Hq=16, Hkv=2, D=64, bs=16, context_lens=(7, 64, 300)),
     dict(seed=114, Hq=4, Hkv=2, D=128, bs=128, context_lens=(1, 128, 129, 1500), partition_size=512),
+    dict(seed=115, Hq=4, Hkv=4, D=64, bs=32, context_lens=(1, 33, 64, 250)),
+    dict(seed=116, Hq=8, Hkv=4, D=128, bs=64, context_lens=(1, 64, 65, 900), kv_dtype="fp8"),
+    dict(seed=117, Hq=2, Hkv=2, D=64, bs=128, context_lens=(3, 128, 129, 1000), kv_dtype="fp8",
+         partition_size=512),
 ]
 
 
