@@ -169,10 +169,10 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int kDL = kD / kWave;         // head-dim values per lane in PV
   constexpr int kQW = kD / 2;             // query dwords (bf16 pairs) per head
   constexpr int kPW = kX / 2;             // weight dwords per V key-chunk
-  // kVM: both products on v_mfma_f32_4x4x4_16b_bf16 (16
-  // independent 4x4x4 blocks per instruction; in block b = lane/4, lane l
-  // holds row l%4 of A, column l%4 of B and of the result), with the K and V
-  // registers used as loaded.
+  // kVM: both products on v_mfma_f32_4x4x4_16b_bf16 (16 independent 4x4x4
+  // blocks per instruction; in block b = lane/4, lane l holds row l%4 of A,
+  // column l%4 of B and of the result), with the K and V registers used as
+  // loaded.
   // * S = Q K^T, four head-dims per step: rows = the query heads, columns =
   //   the block's four keys. Lane l's B operand is its own key's K at those
   //   head-dims, its A operand head l%4's query there (from LDS), and its
@@ -254,8 +254,8 @@ void decode_kernel(const DecodeArgs a) {
     if (kQL > 1) reinterpret_cast<uint4*>(&q_s[0][0])[lane + kWave] = qv1;
   }
   if (kNew && slot_new >= 0) stage_new_token<kD, kFp8>(a, tok, h, lane, tok_s);
-  // (the barrier that publishes blk_s and tok_s comes after the first tile's
-  // loads are issued, below)
+  // (the barrier that publishes blk_s, q_s and tok_s comes after the first
+  // tile's loads are issued, below)
 
   const auto qg = as_constant(
       reinterpret_cast<const uint32_t*>(a.q + ((long long)s * a.num_q_heads + h * kG) * kD));
