@@ -120,6 +120,24 @@ __device__ __forceinline__ void load_row_to_lds(const void* src, void* lds_row) 
   __builtin_amdgcn_global_load_lds(src, lds_row, 16, 0, 0);
 }
 
+// The same copy through a buffer descriptor (buffer_load ... lds, 16 bytes per
+// lane): the lane's bytes are read at base + soff + voff (voff = 16 * lane) and
+// land at lds_row + 16 * lane; offsets at or past `bytes` read zeros. The
+// compiler counts a global_load_lds (FLAT encoding, LDS written) as a pending
+// FLAT access and then waits for every LDS read of the step to complete
+// (lgkmcnt(0)) wherever it waits for one; the buffer form lets the fragment
+// reads of the MFMA loop stay in flight.
+#ifndef PA_PREFILL_COPY_BUFFER
+#define PA_PREFILL_COPY_BUFFER 1
+#endif
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_row_to_lds(__amdgpu_buffer_rsrc_t r, int soff, int voff, void* lds_row) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_row, 16, voff,
+                                           __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
 static constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // kNB = 32-column blocks per wave; a workgroup covers 4 * 32 * kNB packed
@@ -331,6 +349,16 @@ void prefill_kernel(const PrefillArgs a) {
     const int key0 = kt * kBN;
     const int kkey = key0 + k_key < Lk ? key0 + k_key : Lk - 1;
     const int kblk = kBig ? __builtin_amdgcn_readfirstlane(ids.k) : ids.k;
+    if constexpr (kBig && PA_PREFILL_COPY_BUFFER) {
+      // the tile lies in one block: a descriptor over this KV head's slab of it
+      const auto r = copy_rsrc(kpool + (long long)kblk * blk16, int(slab16 * 16));
+#pragma unroll
+      for (int u = 0; u < kKW; ++u) {
+        const int c = w * kKW + u;
+        buffer_row_to_lds(r, ((key0 & bmask) + (c << bshift)) * 16, lane * 16, &ks[c][0]);
+      }
+      return;
+    }
     const uint4* ksrc = kpool + (long long)kblk * blk16 + (kBig ? (key0 & bmask) + k_key : (kkey & bmask));
 #pragma unroll
     for (int u = 0; u < kKW; ++u) {
@@ -342,6 +370,16 @@ void prefill_kernel(const PrefillArgs a) {
   auto issue_v = [&](int kt, const CopyIds& ids, uint4 (*vs)[kD]) {
     const int key0 = kt * kBN;
     const int vblk0 = __builtin_amdgcn_readfirstlane(ids.k);
+    if constexpr (kBig && PA_PREFILL_COPY_BUFFER) {
+      const auto r = copy_rsrc(vpool + (long long)vblk0 * blk16, int(slab16 * 16));
+#pragma unroll
+      for (int u = 0; u < kVW; ++u) {
+        int j, dh;
+        vrow(u, j, dh);
+        buffer_row_to_lds(r, ((((key0 + j * 8) & bmask) >> 3) * kD + dh * 64) * 16, lane * 16, &vs[j][dh * 64]);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < kVW; ++u) {
       int j, dh;
@@ -993,14 +1031,33 @@ void prefill_persist_kernel(const PrefillArgs a, int num_items) {
   auto k_off = [&](int hoff, int t) __attribute__((always_inline)) { return hoff + ((t * kBN) & bmask); };
   auto v_off = [&](int hoff, int t) __attribute__((always_inline)) { return hoff + (((t * kBN) & bmask) >> 3) * kD; };
   auto issue_k = [&](int off, int blk, uint4 (*ks)[kBN]) __attribute__((always_inline)) {
+#if PA_PREFILL_COPY_BUFFER
+    // a descriptor over the block (every KV head's slab; off holds the head's)
+    const auto r = copy_rsrc(kbase + (long long)blk * blk16, blk16 * 16);
+#pragma unroll
+    for (int u = 0; u < kKW; ++u) {
+      const int c = w * kKW + u;
+      buffer_row_to_lds(r, (off + (c << bshift)) * 16, lane * 16, &ks[c][0]);
+    }
+#else
     const uint4* ksrc = kbase + ((long long)blk * blk16 + off) + lane;
 #pragma unroll
     for (int u = 0; u < kKW; ++u) {
       const int c = w * kKW + u;
       load_row_to_lds(ksrc + (c << bshift), &ks[c][0]);
     }
+#endif
   };
   auto issue_v = [&](int off, int blk, uint4 (*vs)[kD]) __attribute__((always_inline)) {
+#if PA_PREFILL_COPY_BUFFER
+    const auto r = copy_rsrc(vbase + (long long)blk * blk16, blk16 * 16);
+#pragma unroll
+    for (int u = 0; u < kVW; ++u) {
+      const int e = w * kVW + u;
+      const int j = e / (kD / 64), dh = e % (kD / 64);
+      buffer_row_to_lds(r, (off + j * kD + dh * 64) * 16, lane * 16, &vs[j][dh * 64]);
+    }
+#else
     const uint4* vb = vbase + ((long long)blk * blk16 + off) + lane;
 #pragma unroll
     for (int u = 0; u < kVW; ++u) {
@@ -1008,6 +1065,7 @@ void prefill_persist_kernel(const PrefillArgs a, int num_items) {
       const int j = e / (kD / 64), dh = e % (kD / 64);
       load_row_to_lds(vb + j * kD + dh * 64, &vs[j][dh * 64]);
     }
+#endif
   };
   // once a V tile with `valid` keys before the end of its item's context has
   // landed in vs (after a barrier), zero the V values of the keys past it: their
