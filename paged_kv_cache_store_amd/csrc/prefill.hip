@@ -58,6 +58,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 #define PA_PREFILL_QK_LEAD 4
 #endif
 
+// LDS fragment reads kept in flight ahead of the MFMAs of a pipelined step
+#ifndef PA_PREFILL_STEP_LEAD
+#define PA_PREFILL_STEP_LEAD 4
+#endif
+
 constexpr int kPrefillThreads = 256;
 constexpr int kPrefillWaves = kPrefillThreads / 64;
 constexpr int kBN = 64;           // keys per tile
@@ -714,7 +719,7 @@ void prefill_kernel(const PrefillArgs a) {
       softmax_exp(s_cur);
       // issue order: a few fragment reads ahead, then each QK^T MFMA followed by
       // a share of the softmax VALU work and the next fragment read
-      constexpr int kQkMfma = 2 * kKS * kNB, kQkReads = 2 * kKS, kLead = 4;
+      constexpr int kQkMfma = 2 * kKS * kNB, kQkReads = 2 * kKS, kLead = PA_PREFILL_STEP_LEAD;
       __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
       for (int i = 0; i < kQkMfma; ++i) {
@@ -1269,7 +1274,7 @@ void prefill_persist_kernel(const PrefillArgs a, int num_items) {
       __builtin_amdgcn_s_setprio(1);
       qk_tile(k_next, s_next);
       softmax_exp(s_cur);
-      constexpr int kQkMfma = 2 * kKS, kQkReads = 2 * kKS, kLead = 4;
+      constexpr int kQkMfma = 2 * kKS, kQkReads = 2 * kKS, kLead = PA_PREFILL_STEP_LEAD;
       __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
       for (int i = 0; i < kQkMfma; ++i) {
