@@ -146,3 +146,20 @@ def test_persistent_random_shapes(set_slots):
             assert np.array_equal(got, ref), f"trial {trial}, slots={n}"
         if trial % 4 == 0:
             assert_close(bf16_f64(ref), _oracle(w), *TOL, what=f"trial {trial}")
+
+
+def test_pool_end_block(set_slots):
+    """A sequence whose last keys sit in the pool's last physical block, with
+    its last 64-key tile running past the context inside that block: the tile
+    copies read only that block's bytes (blocks of 64 and 256 tokens, both
+    launch forms, against the oracle). The pool has one block to spare, the
+    seeds place a sequence's final block last."""
+    import math
+    pf = [(0, 1), (37, 100), (200, 61), (5, 3), (64, 64)]
+    for seed, bs, seq in ((351, 64, 2), (351, 256, 1)):
+        needed = sum(math.ceil((p + c) / bs) for p, c in pf)
+        w = W.custom(seed=seed, Hq=8, Hkv=2, D=128, bs=bs, context_lens=(), prefill=pf, num_blocks=needed + 1)
+        lk = sum(pf[seq])
+        assert w.p_block_tables[seq, math.ceil(lk / bs) - 1] == w.num_blocks - 1 and lk % 64 != 0
+        print(f"seed {seed} block {bs}: sequence {seq} ends in block {w.num_blocks - 1}", flush=True)
+        _check_all_slots(w, set_slots, slots=(0, 1))
