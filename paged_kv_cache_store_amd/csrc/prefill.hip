@@ -14,7 +14,8 @@
 //   so every K/V tile staged in LDS serves all G heads;
 // * K/V tiles of 64 keys are copied from the pool to LDS, double-buffered, in
 //   the pool's own layouts: K [D/8][64 keys][8], V [8 chunks of 8 keys][D][8];
-//   bf16 tiles go straight from the pool into LDS (global_load_lds), fp8 tiles
+//   bf16 tiles go straight from the pool into LDS (buffer_load ... lds with
+//   blocks of at least one tile, else global_load_lds), fp8 tiles
 //   through registers, where they are widened to bf16;
 // * S^T = K Q^T: A = K rows (keys) from LDS, B = Q^T from registers (loaded
 //   once), so each lane owns one query column and its softmax statistics;
@@ -273,7 +274,9 @@ void prefill_kernel(const PrefillArgs a) {
   // loaded before the first tile and moved forward when a tile needs blocks
   // past it. Block sizes are powers of two (shift/mask).
   // bf16 (kDirect): each wave moves whole 1 KB rows of a tile from the pool
-  // into LDS with global_load_lds (16 bytes per lane, lane-major): K rows are
+  // into LDS, 16 bytes per lane, lane-major (buffer_load ... lds through a
+  // descriptor over the tile's block when a tile lies in one block, else
+  // global_load_lds): K rows are
   // (chunk c, 64 keys), V rows (8-key chunk j, 64 head-dims); no staging
   // registers and no LDS writes by the waves. fp8: loads into registers,
   // widening to bf16, LDS writes in the same layouts.
@@ -1029,8 +1032,8 @@ void prefill_persist_kernel(const PrefillArgs a, int num_items) {
     }
   };
 
-  // ---- copies: the pool's rows straight into LDS (global_load_lds, 16 bytes
-  // per lane); with blocks of at least one tile a tile lies in one block, keys
+  // ---- copies: the pool's rows straight into LDS (buffer_load ... lds through
+  // a descriptor over the block, 16 bytes per lane); a tile lies in one block, keys
   // past Lk read slots of that block (in bounds; masked, their V zeroed).
   // Offsets (16-byte units) of tile t of KV head hk inside a block: K rows, V rows
   auto k_off = [&](int hoff, int t) __attribute__((always_inline)) { return hoff + ((t * kBN) & bmask); };
