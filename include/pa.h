@@ -78,7 +78,7 @@ typedef enum { PA_KV_BF16 = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
  * pool are the one exception: stores skip them. */
 
 /* One layer's pool. Supported: block_size in {16,32,64,128,256}, head_dim in
- * {64,128}. For PA_KV_FP8_E4M3, k_scale/v_scale are device float32 arrays of
+ * {64,128}, num_kv_heads at most 1024 (else PA_ERR_UNSUPPORTED). For PA_KV_FP8_E4M3, k_scale/v_scale are device float32 arrays of
  * num_kv_heads dequantisation scales (stored byte b means value(b) * scale[h]);
  * both are ignored (may be NULL) for PA_KV_BF16. */
 typedef struct {

@@ -21,6 +21,8 @@ pa_status hip_status(hipError_t e) {
   return PA_ERR_HIP;
 }
 
+constexpr int kMaxKvHeads = 1024;
+
 bool supported_block_size(int bs) {
   return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
 }
@@ -31,6 +33,8 @@ pa_status check_cache(const pa_cache_desc* c, pa::PoolDims* dims) {
     return PA_ERR_SHAPE;
   if (!supported_block_size(c->block_size)) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // a block (every KV head) stays far below 2 GiB: kernels size it in 32 bits
+  if (c->num_kv_heads > kMaxKvHeads) return PA_ERR_UNSUPPORTED;
   if (c->dtype != PA_KV_BF16 && c->dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
   if (c->dtype == PA_KV_FP8_E4M3 && (!c->k_scale || !c->v_scale)) return PA_ERR_NULL;
   dims->num_blocks = c->num_blocks;
@@ -279,6 +283,7 @@ pa_status pa_prefill_varlen(const void* q, const void* k_cache, const void* v_ca
     if (!cache) return PA_ERR_NULL;
     if (cache->num_kv_heads <= 0 || cache->head_dim <= 0) return PA_ERR_SHAPE;
     if (cache->head_dim != 64 && cache->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (cache->num_kv_heads > kMaxKvHeads) return PA_ERR_UNSUPPORTED;
     if (cache->dtype != PA_KV_BF16) return PA_ERR_UNSUPPORTED;
     dims.num_blocks = 0;
     dims.block_size = 0;

@@ -49,6 +49,7 @@ def test_store_validation(lib):
     assert store(lib, desc(d=96)) == UNSUP
     assert store(lib, desc(dtype=3)) == UNSUP
     assert store(lib, desc(nb=0)) == SHAPE
+    assert store(lib, desc(hkv=1025)) == UNSUP                            # at most 1024 KV heads
     assert store(lib, desc(dtype=1)) == NULL                              # fp8 needs scales
 
 
@@ -140,6 +141,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, desc(dtype=1)) == NULL                         # fp8 needs scales
     assert prefill(lib, desc(dtype=1, ks=FAKE, vs=FAKE), hq=5) == SHAPE
     assert prefill(lib, desc(), mq=-1) == SHAPE
+    assert prefill(lib, desc(hkv=1025), hq=1025) == UNSUP
     assert prefill(lib, desc(), S=0, q=None) == OK
     for bad in (0.0, -0.5, float("inf"), float("nan")):
         assert prefill(lib, desc(), scale=bad) == SHAPE
@@ -160,6 +162,9 @@ def test_prefill_packed_validation(lib):
     d64 = desc()
     d64.head_dim = 96
     assert prefill(lib, d64, bt=None) == UNSUP
+    wide = desc(hkv=1025)
+    wide.num_blocks, wide.block_size = 0, 0
+    assert prefill(lib, wide, bt=None, hq=1025) == UNSUP                  # at most 1024 KV heads
     # with a table, the pool must be a valid one
     assert prefill(lib, nopool) == SHAPE
 
