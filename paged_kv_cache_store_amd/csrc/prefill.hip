@@ -128,7 +128,9 @@ __device__ __forceinline__ void load_row_to_lds(const void* src, void* lds_row) 
 
 // The same copy through a buffer descriptor (buffer_load ... lds, 16 bytes per
 // lane): the lane's bytes are read at base + soff + voff (voff = 16 * lane) and
-// land at lds_row + 16 * lane; offsets at or past `bytes` read zeros. The
+// land at lds_row + 16 * lane. The callers' offsets stay inside the block by
+// construction; the descriptor's size (`bytes`) bounds only voff, the hardware
+// leaving soff out of its range check. The
 // compiler counts a global_load_lds (FLAT encoding, LDS written) as a pending
 // FLAT access and then waits for every LDS read of the step to complete
 // (lgkmcnt(0)) wherever it waits for one; the buffer form lets the fragment
